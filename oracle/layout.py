@@ -1,0 +1,78 @@
+"""Pool geometry and page-table gather for the oracle (test infrastructure only).
+
+Pool layout.  The pages say only that each layer's K and V sit in "blocks" at
+"layout-derived pool offsets" and that the prep checks a "layer offset" and a
+whole-page pool (issue "gemma4: serving prep needs pool-write forms -- hd256 QKV
+in one pass, hd512 V alongside K", Proposed Plan and Acceptance Criteria).  The
+reading taken here, a convention and therefore parity unpinned:
+
+    pool[layer][page][kv][kv_head][slot][dim],   kv = 0 for K, 1 for V,
+
+a flat bf16 buffer of exactly L * N * 2 * H_kv * P * D elements.
+
+Page table.  Attention reads K/V "through a page table" whose addresses come
+from "page ids and the last-page length" (PR "feat(kernels): Rust wrapper for
+the hd256 windowed paged prefill", Description).  Reading: CSR form, request b
+owns ids[indptr[b]:indptr[b+1]] (at least one page) and its KV length is
+(n_pages - 1) * page_size + last_page_len with 1 <= last_page_len <= page_size.
+Logical key j of the request lives at page ids[j // P], slot j % P.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .bf16 import bf16_bits, bits_to_f64
+
+
+@dataclass(frozen=True)
+class PoolGeometry:
+    num_layers: int
+    num_pages: int
+    num_kv_heads: int
+    page_size: int
+    head_dim: int
+
+    @property
+    def shape6(self):
+        return (self.num_layers, self.num_pages, 2, self.num_kv_heads, self.page_size,
+                self.head_dim)
+
+    @property
+    def numel(self) -> int:
+        n = 1
+        for s in self.shape6:
+            n *= s
+        return n
+
+
+def pool6(pool, geom: PoolGeometry) -> np.ndarray:
+    """uint16 view of a flat bf16 pool as [L, N, 2, H_kv, P, D] (no copy for numpy
+    input; one host copy for a torch tensor)."""
+    bits = bf16_bits(pool)
+    if bits.size != geom.numel:
+        raise ValueError(f"pool has {bits.size} elements, geometry needs {geom.numel}")
+    return bits.reshape(geom.shape6)
+
+
+def kv_lengths(kv_page_indptr, kv_last_page_len, page_size: int) -> np.ndarray:
+    """kv_len[b] = (n_pages[b] - 1) * page_size + last_page_len[b]."""
+    indptr = np.asarray(kv_page_indptr, dtype=np.int64)
+    last = np.asarray(kv_last_page_len, dtype=np.int64)
+    n = indptr[1:] - indptr[:-1]
+    return (n - 1) * page_size + last
+
+
+def gather_kv(pool_6d_bits: np.ndarray, layer: int, page_ids, kv_len: int, page_size: int):
+    """Logical K and V of one request, float64 [kv_len, H_kv, D] each.
+
+    Key j is read from page page_ids[j // page_size], slot j % page_size."""
+    page_ids = np.asarray(page_ids, dtype=np.int64)
+    j = np.arange(kv_len, dtype=np.int64)
+    page = page_ids[j // page_size]
+    slot = j % page_size
+    # advanced indices around a slice: the gathered key axis comes first
+    k = pool_6d_bits[layer, page, 0, :, slot, :]
+    v = pool_6d_bits[layer, page, 1, :, slot, :]
+    return bits_to_f64(k), bits_to_f64(v)

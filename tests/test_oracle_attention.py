@@ -1,0 +1,278 @@
+"""Pins for the attention oracle: things other than the oracle itself that fix
+what windowed paged prefill must return (CPU only).
+
+The pages print no worked numbers, so the pins are a hand-derived example
+(tests/golden), a library routine (torch scaled_dot_product_attention in
+float64), brute force on tiny inputs, closed forms and the invariants the
+contract implies (PR "feat(kernels): Rust wrapper for the hd256 windowed paged
+prefill", Description; PR "feat(gemma4): paged KV serving across both attention
+families", Description).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _geom(case):
+    return oracle.PoolGeometry(case.num_layers, case.num_pages, case.num_kv_heads,
+                               case.page_size, case.head_dim)
+
+
+def _run(case, sm_scale=1.0, window_left=-1, pool=None, table=None, samples=None):
+    t = table or case.table
+    return oracle.paged_attention(case.q, case.pool if pool is None else pool, _geom(case),
+                                  case.layer, case.qo_indptr, t.kv_page_indptr,
+                                  t.kv_page_indices, t.kv_last_page_len, sm_scale,
+                                  window_left, samples=samples)
+
+
+def _logical_kv(case):
+    """K, V [kv_len, H, D] per request, read through the page table by a loop
+    over keys that does not use oracle.gather_kv."""
+    g = _geom(case)
+    bits = oracle.bf16_bits(case.pool).reshape(g.shape6)
+    out = []
+    for b in range(len(case.kv_lens)):
+        ids = case.table.kv_page_indices[case.table.kv_page_indptr[b]:case.table.kv_page_indptr[b + 1]]
+        ks, vs = [], []
+        for j in range(case.kv_lens[b]):
+            page, slot = ids[j // case.page_size], j % case.page_size
+            ks.append(oracle.bits_to_f64(bits[case.layer, page, 0, :, slot, :]))
+            vs.append(oracle.bits_to_f64(bits[case.layer, page, 1, :, slot, :]))
+        out.append((np.stack(ks), np.stack(vs)))
+    return out
+
+
+# ---------------------------------------------------------------- golden ----
+
+@pytest.mark.parametrize("window", ["-1", "1", "0"])
+def test_hand_derived_example(window):
+    g = json.load(open(os.path.join(GOLDEN, "attention_tiny.json")))
+    geo = oracle.PoolGeometry(**g["geometry"])
+    pool = torch.tensor(g["pool"], dtype=torch.float32).to(torch.bfloat16)
+    q = torch.tensor(g["q"], dtype=torch.float32).to(torch.bfloat16)
+    o = oracle.paged_attention(q, pool, geo, 0, g["qo_indptr"], g["kv_page_indptr"],
+                               g["kv_page_indices"], g["kv_last_page_len"], math.log(2.0),
+                               int(window))
+    np.testing.assert_allclose(o, np.array(g["expected"][window]), rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------------------ brute force ----
+
+def _brute(q_rows, k, v, pos, scale, window_left):
+    """Per-query loop in plain Python floats: pick keys by the inclusive
+    distance rule, softmax with an explicit max, weighted sum of values."""
+    out = np.zeros_like(q_rows)
+    for i in range(q_rows.shape[0]):
+        keys = [j for j in range(k.shape[0])
+                if pos[i] - j >= 0 and (window_left < 0 or pos[i] - j <= window_left)]
+        sc = [scale * sum(float(a) * float(b) for a, b in zip(q_rows[i], k[j])) for j in keys]
+        mx = max(sc)
+        e = [math.exp(s - mx) for s in sc]
+        z = sum(e)
+        for w, j in zip(e, keys):
+            out[i] += (w / z) * v[j]
+    return out
+
+
+@pytest.mark.parametrize("group", [1, 2, 4])
+@pytest.mark.parametrize("seq", [1, 2, 5, 8])
+def test_brute_force_small(group, seq):
+    h_kv = 2
+    case = synth.attention_case(100 + seq * 10 + group, [seq, max(1, seq - 1)],
+                                [seq, seq + 3], num_qo_heads=h_kv * group,
+                                num_kv_heads=h_kv, head_dim=8, page_size=4, num_pages=9)
+    logical = _logical_kv(case)
+    q = oracle.to_f64(case.q)
+    for wl in range(-1, 9):
+        o = _run(case, sm_scale=0.7, window_left=wl)
+        for b, (k, v) in enumerate(logical):
+            q0, q1 = case.qo_indptr[b], case.qo_indptr[b + 1]
+            pos = case.kv_lens[b] - (q1 - q0) + np.arange(q1 - q0)
+            for h in range(h_kv * group):
+                ref = _brute(q[q0:q1, h], k[:, h // group], v[:, h // group], pos, 0.7, wl)
+                np.testing.assert_allclose(o[q0:q1, h], ref, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------- library SDPA ----
+
+@pytest.mark.parametrize("wl", [-1, 0, 3, 16, 40])
+def test_matches_torch_sdpa_fp64(wl):
+    case = synth.attention_case(7, [33, 1, 20], [50, 17, 20], num_qo_heads=8, num_kv_heads=2,
+                                head_dim=16, page_size=16, num_pages=12)
+    o = _run(case, sm_scale=0.37, window_left=wl)
+    logical = _logical_kv(case)
+    q = oracle.to_f64(case.q)
+    for b, (k, v) in enumerate(logical):
+        q0, q1 = case.qo_indptr[b], case.qo_indptr[b + 1]
+        n_q, n_kv = q1 - q0, case.kv_lens[b]
+        pos = torch.arange(n_kv - n_q, n_kv)[:, None]
+        j = torch.arange(n_kv)[None, :]
+        mask = (pos - j >= 0) & ((pos - j <= wl) if wl >= 0 else torch.ones_like(j, dtype=torch.bool))
+        qt = torch.from_numpy(q[q0:q1]).transpose(0, 1)            # [H, n_q, D]
+        kt = torch.from_numpy(k).transpose(0, 1).repeat_interleave(4, dim=0)
+        vt = torch.from_numpy(v).transpose(0, 1).repeat_interleave(4, dim=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt.contiguous(), vt.contiguous(), attn_mask=mask, scale=0.37)
+        np.testing.assert_allclose(o[q0:q1], ref.transpose(0, 1).numpy(), rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------ closed forms ----
+
+def test_window_zero_returns_own_value():
+    case = synth.attention_case(3, [40], [70], num_qo_heads=4, num_kv_heads=2, head_dim=32,
+                                page_size=16, num_pages=8)
+    o = _run(case, sm_scale=1.0, window_left=0)
+    (k, v), = _logical_kv(case)
+    pos = 70 - 40 + np.arange(40)
+    for h in range(4):
+        np.testing.assert_array_equal(o[:, h], v[pos, h // 2])
+
+
+@pytest.mark.parametrize("wl", [-1, 0, 1, 5, 15, 16, 17, 63])
+def test_uniform_weights_reveal_inclusive_window(wl):
+    """sm_scale = 0 makes every allowed key weigh the same; with one-hot values
+    (V[j] = e_j) the output lists the attended keys: exactly the window_left + 1
+    most recent positions (all earlier ones when window_left = -1)."""
+    kv, qo, d = 64, 24, 64
+    case = synth.attention_case(11, [qo], [kv], num_qo_heads=2, num_kv_heads=1, head_dim=d,
+                                page_size=16, num_pages=4)
+    g = _geom(case)
+    bits = oracle.bf16_bits(case.pool).reshape(g.shape6).copy()
+    ids = case.table.kv_page_indices
+    one = np.uint16(0x3F80)   # bf16 1.0
+    for j in range(kv):
+        bits[0, ids[j // 16], 1, 0, j % 16, :] = 0
+        bits[0, ids[j // 16], 1, 0, j % 16, j] = one
+    o = _run(case, sm_scale=0.0, window_left=wl, pool=bits.reshape(-1))
+    for i in range(qo):
+        p = kv - qo + i
+        lo = 0 if wl < 0 else max(0, p - wl)
+        want = np.zeros(d)
+        want[lo:p + 1] = 1.0 / (p + 1 - lo)
+        for h in range(2):
+            np.testing.assert_allclose(o[i, h], want, rtol=0, atol=1e-15)
+
+
+def test_constant_values_give_constant_output():
+    case = synth.attention_case(5, [30, 9], [45, 9], num_qo_heads=4, num_kv_heads=4,
+                                head_dim=16, page_size=8, num_pages=9)
+    g = _geom(case)
+    bits = oracle.bf16_bits(case.pool).reshape(g.shape6).copy()
+    bits[:, :, 1] = np.uint16(0x3FC0)   # bf16 1.5 everywhere in V
+    o = _run(case, sm_scale=2.0, window_left=7, pool=bits.reshape(-1))
+    np.testing.assert_allclose(o, 1.5, rtol=0, atol=1e-14)
+
+
+# -------------------------------------------------------------- invariants ----
+
+def test_page_permutation_invariance():
+    """Moving every page to another physical slot of the pool (and remapping the
+    table) changes nothing: paging is pure addressing."""
+    case = synth.attention_case(21, [37, 64, 5], [100, 64, 77], num_qo_heads=4,
+                                num_kv_heads=2, head_dim=32, page_size=16, num_pages=40)
+    base = _run(case, window_left=20)
+    g = _geom(case)
+    bits = oracle.bf16_bits(case.pool).reshape(g.shape6)
+    perm = np.random.default_rng(0).permutation(g.num_pages)
+    moved = np.empty_like(bits)
+    moved[:, perm] = bits                  # page p now lives at perm[p]
+    t = case.table
+    t2 = synth.PageTable(t.kv_page_indptr, perm[t.kv_page_indices].astype(np.int32),
+                         t.kv_last_page_len)
+    out = _run(case, window_left=20, pool=moved.reshape(-1), table=t2)
+    np.testing.assert_array_equal(out, base)
+
+
+def test_saturated_window_equals_full_causal():
+    case = synth.attention_case(8, [50, 3], [90, 40], num_qo_heads=4, num_kv_heads=1,
+                                head_dim=16, page_size=16, num_pages=10)
+    full = _run(case, window_left=-1)
+    for wl in (89, 90, 1000, 10 ** 6):
+        np.testing.assert_array_equal(_run(case, window_left=wl), full)
+    assert not np.array_equal(_run(case, window_left=88), full)
+
+
+def test_gqa_replicated_heads():
+    """Copying KV head g into heads g*group .. g*group+group-1 and running with
+    one query head per KV head reproduces the grouped result (the group is the
+    integer quotient H_q / H_kv, heads taken in contiguous blocks)."""
+    group, h_kv = 4, 2
+    case = synth.attention_case(31, [20], [45], num_qo_heads=group * h_kv, num_kv_heads=h_kv,
+                                head_dim=16, page_size=16, num_pages=3)
+    base = _run(case, sm_scale=0.8, window_left=9)
+    g = _geom(case)
+    bits = oracle.bf16_bits(case.pool).reshape(g.shape6)
+    rep = np.repeat(bits, group, axis=3)
+    g2 = oracle.PoolGeometry(g.num_layers, g.num_pages, h_kv * group, g.page_size, g.head_dim)
+    t = case.table
+    out = oracle.paged_attention(case.q, rep.reshape(-1), g2, 0, case.qo_indptr,
+                                 t.kv_page_indptr, t.kv_page_indices, t.kv_last_page_len,
+                                 0.8, 9)
+    np.testing.assert_array_equal(out, base)
+
+
+@pytest.mark.parametrize("wl", [-1, 6])
+def test_decode_equals_prefill_row(wl):
+    """A one-token call whose KV ends at position p gives row p of the prefill
+    over the same pages (decode runs through the prefill entry at one token)."""
+    kv = 40
+    case = synth.attention_case(41, [kv], [kv], num_qo_heads=2, num_kv_heads=1, head_dim=16,
+                                page_size=8, num_pages=5)
+    full = _run(case, sm_scale=1.0, window_left=wl)
+    ids = case.table.kv_page_indices
+    for p in (0, 7, 8, 9, 39):
+        n_pages = p // 8 + 1
+        t = synth.PageTable(np.array([0, n_pages], np.int32), ids[:n_pages].copy(),
+                            np.array([p - (n_pages - 1) * 8 + 1], np.int32))
+        q1 = case.q[p:p + 1]
+        o = oracle.paged_attention(q1, case.pool, _geom(case), 0, np.array([0, 1], np.int32),
+                                   t.kv_page_indptr, t.kv_page_indices, t.kv_last_page_len,
+                                   1.0, wl)
+        np.testing.assert_allclose(o[0], full[p], rtol=0, atol=1e-13)
+
+
+def test_sampled_rows_match_full():
+    case = synth.attention_case(55, [30, 12], [30, 50], num_qo_heads=4, num_kv_heads=2,
+                                head_dim=16, page_size=16, num_pages=6)
+    full = _run(case, window_left=10)
+    samples = [(0, 0), (29, 3), (30, 1), (41, 2)]
+    part = _run(case, window_left=10, samples=samples)
+    for tok, h in samples:
+        np.testing.assert_allclose(part[tok, h], full[tok, h], rtol=0, atol=1e-13)
+
+
+def test_unused_pages_and_tail_slots_are_never_read():
+    """NaN in pages outside the table and in slots past last_page_len leaves the
+    output unchanged."""
+    case = synth.attention_case(61, [20, 7], [37, 7], num_qo_heads=2, num_kv_heads=1,
+                                head_dim=16, page_size=16, num_pages=8)
+    base = _run(case, window_left=-1)
+    g = _geom(case)
+    bits = oracle.bf16_bits(case.pool).reshape(g.shape6).copy()
+    used = set(case.table.kv_page_indices.tolist())
+    for p in range(g.num_pages):
+        if p not in used:
+            bits[:, p] = np.uint16(0x7FA5)
+    t = case.table
+    for b in range(2):
+        last_page = t.kv_page_indices[t.kv_page_indptr[b + 1] - 1]
+        bits[0, last_page, :, :, t.kv_last_page_len[b]:, :] = np.uint16(0x7FA5)
+    out = _run(case, window_left=-1, pool=bits.reshape(-1))
+    np.testing.assert_array_equal(out, base)
+
+
+def test_rejects_bad_window():
+    case = synth.attention_case(1, [2], [2], num_qo_heads=1, num_kv_heads=1, head_dim=4,
+                                page_size=2, num_pages=1)
+    with pytest.raises(ValueError):
+        _run(case, window_left=-2)
