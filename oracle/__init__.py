@@ -29,7 +29,7 @@ eps, and the RoPE pairing, whose frequency schedule and pairing are pinned only
 against a library routine).
 """
 from .bf16 import bf16_bits, bits_to_f64, to_f64, f64_to_bf16_bits, ulp_bf16
-from .layout import PoolGeometry, pool6, gather_kv, kv_lengths
+from .layout import PoolGeometry, kv_blocks, gather_kv, kv_lengths
 from .attention import paged_attention, attention_rows, allowed_keys
 from .prep import (inv_rms, rms_norm_weighted, rope_rotate_half, qkv_prep_hd256,
                    kv_prep_hd512, token_positions, expected_pool_writes,
@@ -37,7 +37,7 @@ from .prep import (inv_rms, rms_norm_weighted, rope_rotate_half, qkv_prep_hd256,
 
 __all__ = [
     "bf16_bits", "bits_to_f64", "to_f64", "f64_to_bf16_bits", "ulp_bf16",
-    "PoolGeometry", "pool6", "gather_kv", "kv_lengths",
+    "PoolGeometry", "kv_blocks", "gather_kv", "kv_lengths",
     "paged_attention", "attention_rows", "allowed_keys",
     "inv_rms", "rms_norm_weighted", "rope_rotate_half", "qkv_prep_hd256",
     "kv_prep_hd512", "token_positions", "expected_pool_writes", "apply_pool_writes",

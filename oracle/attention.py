@@ -31,7 +31,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .layout import PoolGeometry, pool6, gather_kv, kv_lengths
+from .layout import PoolGeometry, kv_blocks, gather_kv, kv_lengths
 from .bf16 import to_f64
 
 
@@ -78,7 +78,7 @@ def paged_attention(q, pool, geom: PoolGeometry, layer: int, qo_indptr, kv_page_
     group = h_q // h_kv
     if d != geom.head_dim:
         raise ValueError("head_dim mismatch")
-    p6 = pool6(pool, geom)
+    kblk, vblk = kv_blocks(pool, geom)
     qo_indptr = np.asarray(qo_indptr, dtype=np.int64)
     kv_page_indptr = np.asarray(kv_page_indptr, dtype=np.int64)
     kv_page_indices = np.asarray(kv_page_indices, dtype=np.int64)
@@ -102,7 +102,7 @@ def paged_attention(q, pool, geom: PoolGeometry, layer: int, qo_indptr, kv_page_
         if qo_len < 1 or n_kv < qo_len:
             raise ValueError(f"request {b}: qo_len {qo_len}, kv_len {n_kv}")
         pages = kv_page_indices[kv_page_indptr[b]:kv_page_indptr[b + 1]]
-        k, v = gather_kv(p6, layer, pages, n_kv, geom.page_size)
+        k, v = gather_kv(kblk, vblk, layer, pages, n_kv, geom.page_size)
         start = n_kv - qo_len
         if want is None:
             pos = start + np.arange(qo_len, dtype=np.int64)

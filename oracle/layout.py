@@ -6,9 +6,11 @@ whole-page pool (issue "gemma4: serving prep needs pool-write forms -- hd256 QKV
 in one pass, hd512 V alongside K", Proposed Plan and Acceptance Criteria).  The
 reading taken here, a convention and therefore parity unpinned:
 
-    pool[layer][page][kv][kv_head][slot][dim],   kv = 0 for K, 1 for V,
+    per (layer, page): a K block [kv_head][slot][dim], then a V block
+    [kv_head][dim][slot] (dim-major: keys contiguous for each dim),
 
-a flat bf16 buffer of exactly L * N * 2 * H_kv * P * D elements.
+a flat bf16 buffer of exactly L * N * 2 * H_kv * P * D elements, layers outer,
+pages next.
 
 Page table.  Attention reads K/V "through a page table" whose addresses come
 from "page ids and the last-page length" (PR "feat(kernels): Rust wrapper for
@@ -35,25 +37,28 @@ class PoolGeometry:
     head_dim: int
 
     @property
-    def shape6(self):
-        return (self.num_layers, self.num_pages, 2, self.num_kv_heads, self.page_size,
-                self.head_dim)
+    def block(self) -> int:
+        """Elements of one K (or V) block of one page."""
+        return self.num_kv_heads * self.page_size * self.head_dim
 
     @property
     def numel(self) -> int:
-        n = 1
-        for s in self.shape6:
-            n *= s
-        return n
+        return self.num_layers * self.num_pages * 2 * self.block
 
 
-def pool6(pool, geom: PoolGeometry) -> np.ndarray:
-    """uint16 view of a flat bf16 pool as [L, N, 2, H_kv, P, D] (no copy for numpy
-    input; one host copy for a torch tensor)."""
-    bits = bf16_bits(pool)
-    if bits.size != geom.numel:
-        raise ValueError(f"pool has {bits.size} elements, geometry needs {geom.numel}")
-    return bits.reshape(geom.shape6)
+def kv_blocks(pool, geom: PoolGeometry):
+    """(K, V) views of a flat pool (uint16 bits, or any numpy array):
+    K [L, N, H, P, D] and V [L, N, H, D, P]."""
+    arr = bf16_bits(pool) if not isinstance(pool, np.ndarray) or pool.dtype == np.uint16 else pool
+    if arr.size != geom.numel:
+        raise ValueError(f"pool has {arr.size} elements, geometry needs {geom.numel}")
+    g = geom
+    pages = arr.reshape(g.num_layers, g.num_pages, 2, g.block)
+    k = pages[:, :, 0, :].reshape(g.num_layers, g.num_pages, g.num_kv_heads, g.page_size,
+                                  g.head_dim)
+    v = pages[:, :, 1, :].reshape(g.num_layers, g.num_pages, g.num_kv_heads, g.head_dim,
+                                  g.page_size)
+    return k, v
 
 
 def kv_lengths(kv_page_indptr, kv_last_page_len, page_size: int) -> np.ndarray:
@@ -64,7 +69,8 @@ def kv_lengths(kv_page_indptr, kv_last_page_len, page_size: int) -> np.ndarray:
     return (n - 1) * page_size + last
 
 
-def gather_kv(pool_6d_bits: np.ndarray, layer: int, page_ids, kv_len: int, page_size: int):
+def gather_kv(kblk: np.ndarray, vblk: np.ndarray, layer: int, page_ids, kv_len: int,
+              page_size: int):
     """Logical K and V of one request, float64 [kv_len, H_kv, D] each.
 
     Key j is read from page page_ids[j // page_size], slot j % page_size."""
@@ -73,6 +79,6 @@ def gather_kv(pool_6d_bits: np.ndarray, layer: int, page_ids, kv_len: int, page_
     page = page_ids[j // page_size]
     slot = j % page_size
     # advanced indices around a slice: the gathered key axis comes first
-    k = pool_6d_bits[layer, page, 0, :, slot, :]
-    v = pool_6d_bits[layer, page, 1, :, slot, :]
+    k = kblk[layer, page, :, slot, :]          # [kv_len, H, D]
+    v = vblk[layer, page, :, :, slot]          # [kv_len, H, D]
     return bits_to_f64(k), bits_to_f64(v)

@@ -31,7 +31,7 @@ from __future__ import annotations
 import numpy as np
 
 from .bf16 import to_f64
-from .layout import PoolGeometry, pool6, kv_lengths
+from .layout import PoolGeometry, kv_blocks, kv_lengths
 
 
 def inv_rms(x: np.ndarray, eps: float) -> np.ndarray:
@@ -107,12 +107,16 @@ def expected_pool_writes(geom: PoolGeometry, layer: int, qo_indptr, kv_page_indp
     return page, slot
 
 
-def apply_pool_writes(pool_f64_6d: np.ndarray, layer: int, page, slot, k_rows, v_rows):
-    """Write K/V rows into a float64 [L, N, 2, H, P, D] pool copy, in place.
-    Returns a boolean mask of the elements written."""
-    mask = np.zeros(pool_f64_6d.shape, dtype=bool)
+def apply_pool_writes(pool_f64: np.ndarray, geom: PoolGeometry, layer: int, page, slot,
+                      k_rows, v_rows):
+    """Write K/V rows into a flat float64 pool copy (layout of ``oracle.layout``),
+    in place.  Returns a flat boolean mask of the elements written."""
+    kb, vb = kv_blocks(pool_f64, geom)
+    mask = np.zeros(pool_f64.shape, dtype=bool)
+    mk, mv = kv_blocks(mask, geom)
     for t in range(len(page)):
-        pool_f64_6d[layer, page[t], 0, :, slot[t], :] = k_rows[t]
-        pool_f64_6d[layer, page[t], 1, :, slot[t], :] = v_rows[t]
-        mask[layer, page[t], :, :, slot[t], :] = True
+        kb[layer, page[t], :, slot[t], :] = k_rows[t]
+        vb[layer, page[t], :, :, slot[t]] = v_rows[t]
+        mk[layer, page[t], :, slot[t], :] = True
+        mv[layer, page[t], :, :, slot[t]] = True
     return mask

@@ -35,20 +35,35 @@ def _run(case, sm_scale=1.0, window_left=-1, pool=None, table=None, samples=None
                                   window_left, samples=samples)
 
 
-def _logical_kv(case):
-    """K, V [kv_len, H, D] per request, read through the page table by a loop
-    over keys that does not use oracle.gather_kv."""
+def _flat_k(g, layer, page, head, slot, d):
+    """Flat index of a K element: per (layer, page) a K block [H][P][D] then a V block."""
+    blk = g.num_kv_heads * g.page_size * g.head_dim
+    return ((layer * g.num_pages + page) * 2) * blk + (head * g.page_size + slot) * g.head_dim + d
+
+
+def _flat_v(g, layer, page, head, d, slot):
+    """Flat index of a V element: the V block is dim-major, [H][D][P]."""
+    blk = g.num_kv_heads * g.page_size * g.head_dim
+    return ((layer * g.num_pages + page) * 2 + 1) * blk + (head * g.head_dim + d) * g.page_size + slot
+
+
+def _logical_kv(case, pool=None):
+    """K, V [kv_len, H, D] per request, read element by element through the page
+    table with flat indices (independent of oracle.gather_kv / kv_blocks)."""
     g = _geom(case)
-    bits = oracle.bf16_bits(case.pool).reshape(g.shape6)
+    bits = oracle.bf16_bits(case.pool if pool is None else pool).reshape(-1)
+    d = np.arange(g.head_dim)
     out = []
     for b in range(len(case.kv_lens)):
         ids = case.table.kv_page_indices[case.table.kv_page_indptr[b]:case.table.kv_page_indptr[b + 1]]
         ks, vs = [], []
         for j in range(case.kv_lens[b]):
             page, slot = ids[j // case.page_size], j % case.page_size
-            ks.append(oracle.bits_to_f64(bits[case.layer, page, 0, :, slot, :]))
-            vs.append(oracle.bits_to_f64(bits[case.layer, page, 1, :, slot, :]))
-        out.append((np.stack(ks), np.stack(vs)))
+            ks.append([oracle.bits_to_f64(bits[_flat_k(g, case.layer, page, hh, slot, d)])
+                       for hh in range(g.num_kv_heads)])
+            vs.append([oracle.bits_to_f64(bits[_flat_v(g, case.layer, page, hh, d, slot)])
+                       for hh in range(g.num_kv_heads)])
+        out.append((np.array(ks), np.array(vs)))
     return out
 
 
@@ -147,13 +162,13 @@ def test_uniform_weights_reveal_inclusive_window(wl):
     case = synth.attention_case(11, [qo], [kv], num_qo_heads=2, num_kv_heads=1, head_dim=d,
                                 page_size=16, num_pages=4)
     g = _geom(case)
-    bits = oracle.bf16_bits(case.pool).reshape(g.shape6).copy()
+    bits = oracle.bf16_bits(case.pool).copy()
     ids = case.table.kv_page_indices
     one = np.uint16(0x3F80)   # bf16 1.0
     for j in range(kv):
-        bits[0, ids[j // 16], 1, 0, j % 16, :] = 0
-        bits[0, ids[j // 16], 1, 0, j % 16, j] = one
-    o = _run(case, sm_scale=0.0, window_left=wl, pool=bits.reshape(-1))
+        bits[_flat_v(g, 0, ids[j // 16], 0, np.arange(d), j % 16)] = 0
+        bits[_flat_v(g, 0, ids[j // 16], 0, j, j % 16)] = one
+    o = _run(case, sm_scale=0.0, window_left=wl, pool=bits)
     for i in range(qo):
         p = kv - qo + i
         lo = 0 if wl < 0 else max(0, p - wl)
@@ -167,9 +182,9 @@ def test_constant_values_give_constant_output():
     case = synth.attention_case(5, [30, 9], [45, 9], num_qo_heads=4, num_kv_heads=4,
                                 head_dim=16, page_size=8, num_pages=9)
     g = _geom(case)
-    bits = oracle.bf16_bits(case.pool).reshape(g.shape6).copy()
-    bits[:, :, 1] = np.uint16(0x3FC0)   # bf16 1.5 everywhere in V
-    o = _run(case, sm_scale=2.0, window_left=7, pool=bits.reshape(-1))
+    bits = oracle.bf16_bits(case.pool).copy()
+    bits.reshape(g.num_layers, g.num_pages, 2, -1)[:, :, 1] = np.uint16(0x3FC0)  # 1.5 in V
+    o = _run(case, sm_scale=2.0, window_left=7, pool=bits)
     np.testing.assert_allclose(o, 1.5, rtol=0, atol=1e-14)
 
 
@@ -182,7 +197,7 @@ def test_page_permutation_invariance():
                                 num_kv_heads=2, head_dim=32, page_size=16, num_pages=40)
     base = _run(case, window_left=20)
     g = _geom(case)
-    bits = oracle.bf16_bits(case.pool).reshape(g.shape6)
+    bits = oracle.bf16_bits(case.pool).reshape(g.num_layers, g.num_pages, -1)
     perm = np.random.default_rng(0).permutation(g.num_pages)
     moved = np.empty_like(bits)
     moved[:, perm] = bits                  # page p now lives at perm[p]
@@ -211,8 +226,10 @@ def test_gqa_replicated_heads():
                                 head_dim=16, page_size=16, num_pages=3)
     base = _run(case, sm_scale=0.8, window_left=9)
     g = _geom(case)
-    bits = oracle.bf16_bits(case.pool).reshape(g.shape6)
-    rep = np.repeat(bits, group, axis=3)
+    kb, vb = oracle.kv_blocks(case.pool, g)
+    kr = np.repeat(kb, group, axis=2).reshape(g.num_layers, g.num_pages, 1, -1)
+    vr = np.repeat(vb, group, axis=2).reshape(g.num_layers, g.num_pages, 1, -1)
+    rep = np.concatenate([kr, vr], axis=2)
     g2 = oracle.PoolGeometry(g.num_layers, g.num_pages, h_kv * group, g.page_size, g.head_dim)
     t = case.table
     out = oracle.paged_attention(case.q, rep.reshape(-1), g2, 0, case.qo_indptr,
@@ -258,16 +275,20 @@ def test_unused_pages_and_tail_slots_are_never_read():
                                 head_dim=16, page_size=16, num_pages=8)
     base = _run(case, window_left=-1)
     g = _geom(case)
-    bits = oracle.bf16_bits(case.pool).reshape(g.shape6).copy()
+    bits = oracle.bf16_bits(case.pool).copy()
     used = set(case.table.kv_page_indices.tolist())
+    by_page = bits.reshape(g.num_layers, g.num_pages, -1)
     for p in range(g.num_pages):
         if p not in used:
-            bits[:, p] = np.uint16(0x7FA5)
+            by_page[:, p] = np.uint16(0x7FA5)
     t = case.table
     for b in range(2):
         last_page = t.kv_page_indices[t.kv_page_indptr[b + 1] - 1]
-        bits[0, last_page, :, :, t.kv_last_page_len[b]:, :] = np.uint16(0x7FA5)
-    out = _run(case, window_left=-1, pool=bits.reshape(-1))
+        for slot in range(t.kv_last_page_len[b], g.page_size):
+            for hh in range(g.num_kv_heads):
+                bits[_flat_k(g, 0, last_page, hh, slot, np.arange(g.head_dim))] = np.uint16(0x7FA5)
+                bits[_flat_v(g, 0, last_page, hh, np.arange(g.head_dim), slot)] = np.uint16(0x7FA5)
+    out = _run(case, window_left=-1, pool=bits)
     np.testing.assert_array_equal(out, base)
 
 

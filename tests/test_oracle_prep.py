@@ -149,7 +149,7 @@ def test_hd512_unit_weight_position_zero_gives_k_equal_v():
 
 def test_scatter_then_gather_roundtrip():
     """Rows written at slot start_pos + t read back, through the page table, as
-    keys start_pos .. start_pos + n - 1 of each request."""
+    keys start_pos .. start_pos + n - 1 of each request; nothing else is written."""
     case = synth.prep_case(12, [5, 33, 16], [11, 0, 48], head_dim=8, num_kv_heads=2,
                            num_layers=3, layer=1, extra_pages=4)
     g = oracle.PoolGeometry(case.num_layers, case.num_pages, 2, case.page_size, 8)
@@ -157,12 +157,16 @@ def test_scatter_then_gather_roundtrip():
     page, slot = oracle.expected_pool_writes(g, 1, case.qo_indptr, t.kv_page_indptr,
                                              t.kv_page_indices, t.kv_last_page_len)
     n = len(page)
-    k_rows = np.arange(n * 2 * 8, dtype=np.float64).reshape(n, 2, 8)
+    k_rows = np.arange(n * 2 * 8, dtype=np.float64).reshape(n, 2, 8) + 1.0
     v_rows = -k_rows
-    pool = np.zeros(g.shape6)
-    mask = oracle.apply_pool_writes(pool, 1, page, slot, k_rows, v_rows)
-    assert mask.sum() == n * 2 * 2 * 8
-    assert not mask[0].any() and not mask[2].any()
+    pool = np.zeros(g.numel)
+    mask = oracle.apply_pool_writes(pool, g, 1, page, slot, k_rows, v_rows)
+    assert mask.sum() == n * 2 * 2 * 8 == np.count_nonzero(pool)
+    per_layer = mask.reshape(3, -1)
+    assert not per_layer[0].any() and not per_layer[2].any()
+    # read back with flat indices: K block [H][P][D], V block [H][D][P]
+    blk = 2 * 16 * 8
+    d = np.arange(8)
     pos = oracle.token_positions(case.qo_indptr, t.kv_page_indptr, t.kv_last_page_len, 16)
     for b in range(3):
         q0, q1 = case.qo_indptr[b], case.qo_indptr[b + 1]
@@ -170,8 +174,11 @@ def test_scatter_then_gather_roundtrip():
         for tok in range(q0, q1):
             p = pos[tok]
             assert p == [11, 0, 48][b] + tok - q0
-            np.testing.assert_array_equal(pool[1, ids[p // 16], 0, :, p % 16, :], k_rows[tok])
-            np.testing.assert_array_equal(pool[1, ids[p // 16], 1, :, p % 16, :], v_rows[tok])
+            base = (1 * g.num_pages + ids[p // 16]) * 2 * blk
+            for hh in range(2):
+                np.testing.assert_array_equal(pool[base + (hh * 16 + p % 16) * 8 + d], k_rows[tok, hh])
+                np.testing.assert_array_equal(pool[base + blk + (hh * 8 + d) * 16 + p % 16],
+                                              v_rows[tok, hh])
 
 
 def test_bf16_helpers():
