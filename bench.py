@@ -1,0 +1,329 @@
+"""Benchmark of the paged sliding-window hot path on one MI355X.
+
+One step runs every row of the hot path once, each on its own seeded synthetic
+workload (inputs resident in HBM before timing starts), all on one stream:
+
+  prep_hd256           fused Q/K/V norm+RoPE+scatter, 8192 tokens, layer 3 of 8
+  prep_hd512           fused K/V (V = weightless norm of raw K), 8192 tokens
+  prefill_window_hd256 windowed paged prefill, 8 requests ~ U[128, 2048], window 1023
+  prefill_hd512        full paged prefill, 4 x 4096 tokens, 16 Q / 1 KV heads
+  decode_local_hd256   one-token decode through the prefill entry, 64 requests,
+                       KV ~ U[512, 8192], window 1023
+  decode_global_hd512  the same requests on the global family, full attention
+
+Each kernel launch is bracketed by HIP events on that stream; a 1 GiB buffer is
+rewritten before every HBM-bound row (outside its events) so its bytes come
+from HBM, not from the 256 MB last-level cache.
+
+The JSON line's `value` is the windowed paged prefill's algorithmic TFLOP/s on
+the batch-8 workload (only (query, key) pairs inside the window count).  Per-row
+figures (TFLOP/s against the bf16 MFMA peak, GB/s against HBM) are under
+`rows`; `cpu_baseline` times the fp64 oracle on a bounded sample of the same
+workload on this host.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--rows a,b] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "windowed paged prefill TFLOP/s (% MFMA peak); seq_len-1 decode KV GB/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ algorithmic work ----
+
+def attention_flops(qo_lens, kv_lens, num_qo_heads, head_dim, window_left):
+    """4 * D * H_q * sum over queries of the number of visible keys."""
+    pairs = 0
+    for qo, kv in zip(qo_lens, kv_lens):
+        p = np.arange(kv - qo, kv, dtype=np.int64)
+        vis = p + 1 if window_left < 0 else np.minimum(p, window_left) + 1
+        pairs += int(vis.sum())
+    return 4.0 * head_dim * num_qo_heads * pairs
+
+
+def decode_bytes(kv_lens, num_qo_heads, num_kv_heads, head_dim, window_left, page_size=16):
+    keys = 0
+    pages = 0
+    for kv in kv_lens:
+        n = kv if window_left < 0 else min(kv, window_left + 1)
+        keys += n
+        pages += (n + page_size - 1) // page_size + 1
+    kvb = keys * num_kv_heads * head_dim * 2 * 2
+    qo = len(kv_lens) * num_qo_heads * head_dim * 2 * 2
+    return float(kvb + qo + pages * 4)
+
+
+def prep_bytes(tokens, head_dim, hq, hkv, with_q_v):
+    half = head_dim // 2
+    tables = tokens * half * 4 * 2
+    if with_q_v:
+        rd = tokens * (hq + 2 * hkv) * head_dim * 2
+        wr = tokens * (hq + 2 * hkv) * head_dim * 2
+        w = 2 * head_dim * 2
+    else:
+        rd = tokens * hkv * head_dim * 2
+        wr = tokens * 2 * hkv * head_dim * 2
+        w = head_dim * 2
+    return float(rd + wr + tables + w)
+
+
+# ------------------------------------------------------------------ workloads ----
+
+class Row:
+    def __init__(self, name, run, work, unit, bound, desc, hbm=False):
+        self.name, self.run, self.work, self.unit = name, run, work, unit
+        self.bound, self.desc, self.hbm = bound, desc, hbm
+
+
+def build_rows(torch, psw, synth, dev, want):
+    rows = []
+    stream = torch.cuda.current_stream()
+
+    def plan_of(qo_indptr, table, hq, hkv, d, num_pages):
+        return psw.Plan(qo_indptr, table.kv_page_indptr, table.kv_page_indices,
+                        table.kv_last_page_len, num_qo_heads=hq, num_kv_heads=hkv, head_dim=d,
+                        page_size=16, num_pages=num_pages, stream=stream)
+
+    def tables(d):
+        c = torch.empty(16384, d // 2, dtype=torch.float32, device=dev)
+        s = torch.empty_like(c)
+        psw.rope_tables(c, s, 16384, d, 1e4)
+        return c, s
+
+    # ---- prep (8192 tokens, start 0, layer 3 of 8, 1024-page pools) ----
+    if "prep_hd256" in want or "prep_hd512" in want:
+        for d, name in ((256, "prep_hd256"), (512, "prep_hd512")):
+            if name not in want:
+                continue
+            hkv = 8 if d == 256 else 1
+            case = synth.prep_case(4, [8192], [0], head_dim=d, num_kv_heads=hkv, num_layers=8,
+                                   layer=3, num_pages=1024, with_q_v=(d == 256))
+            numel = 8 * 1024 * 2 * hkv * 16 * d
+            pool = torch.zeros(numel, dtype=torch.bfloat16, device=dev)
+            pd = psw.pool_desc(pool, num_layers=8, num_pages=1024, page_size=16,
+                               num_kv_heads=hkv, head_dim=d)
+            plan = plan_of(case.qo_indptr, case.table, 16, hkv, d, 1024)
+            c, s = tables(d)
+            k_in = case.k_in.to(dev)
+            k_w = case.k_norm_w.to(dev)
+            if d == 256:
+                q_in, v_in = case.q_in.to(dev), case.v_in.to(dev)
+                q_w = case.q_norm_w.to(dev)
+                q_out = torch.empty_like(q_in)
+
+                def run(plan=plan, pd=pd, q_in=q_in, k_in=k_in, v_in=v_in, q_w=q_w, k_w=k_w,
+                        c=c, s=s, q_out=q_out):
+                    psw.qkv_norm_rope_paged_prefill_hd256(plan, pd, 3, q_in, k_in, v_in, q_w,
+                                                          k_w, c, s, 1e-6, q_out)
+            else:
+                def run(plan=plan, pd=pd, k_in=k_in, k_w=k_w, c=c, s=s):
+                    psw.k_v_norm_rope_paged_prefill_hd512(plan, pd, 3, k_in, k_w, c, s, 1e-6)
+            work = prep_bytes(8192, d, 16, hkv, d == 256)
+            rows.append(Row(name, run, work, "GB/s", "hbm",
+                            f"fused prep hd{d}, 8192 tokens at start 0, layer 3 of 8, "
+                            f"1024-page pool, RoPE theta 1e4 over 16384 positions", hbm=True))
+
+    # ---- windowed prefill hd256, batch 8 ----
+    if "prefill_window_hd256" in want:
+        lens = synth.uniform_lengths(8, 128, 2048, synth.generator(2))
+        case = synth.attention_case(2, lens, lens, num_pages=4096, **synth.LOCAL)
+        pool = case.pool.to(dev)
+        q = case.q.to(dev)
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        plan = plan_of(case.qo_indptr, case.table, 16, 8, 256, 4096)
+        pd = psw.pool_desc(pool, num_layers=1, num_pages=4096, page_size=16, num_kv_heads=8,
+                           head_dim=256)
+
+        def run(plan=plan, pd=pd, q=q, o=o):
+            psw.paged_prefill_window_hd256(plan, pd, 0, q, 1.0, 1023, o)
+        rows.append(Row("prefill_window_hd256", run,
+                        attention_flops(lens, lens, 16, 256, 1023), "TFLOP/s", "mfma",
+                        f"hd256 windowed paged prefill, batch 8, seq_len {lens}, 16Q/8KV, "
+                        f"page 16, pool 4096 pages, window_left 1023, sm_scale 1, bf16 out"))
+        rows[-1].case = case
+
+    # ---- full prefill hd512, 4 x 4096 ----
+    if "prefill_hd512" in want:
+        case = synth.attention_case(3, [4096] * 4, [4096] * 4, num_pages=2048, fill_pool=False,
+                                    **synth.GLOBAL)
+        # fill the pool the way serving does: the hd512 prep writes K and V
+        # (V = weightless norm of the raw K) from raw K ~ N(0, 0.25^2)
+        pool = torch.zeros(case.pool.numel(), dtype=torch.bfloat16, device=dev)
+        pd = psw.pool_desc(pool, num_layers=1, num_pages=2048, page_size=16, num_kv_heads=1,
+                           head_dim=512)
+        plan = plan_of(case.qo_indptr, case.table, 16, 1, 512, 2048)
+        raw_k = synth.normal_bf16((16384, 1, 512), 0.25, synth.generator(33), device=dev)
+        w = torch.ones(512, dtype=torch.bfloat16, device=dev)
+        c, s = tables(512)
+        psw.k_v_norm_rope_paged_prefill_hd512(plan, pd, 0, raw_k, w, c, s, 1e-6)
+        q = case.q.to(dev)
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+
+        def run(plan=plan, pd=pd, q=q, o=o):
+            psw.paged_prefill_hd512(plan, pd, 0, q, 1.0, o)
+        rows.append(Row("prefill_hd512", run,
+                        attention_flops([4096] * 4, [4096] * 4, 16, 512, -1), "TFLOP/s", "mfma",
+                        "hd512 full paged prefill, 4 x 4096 tokens, 16Q/1KV, causal, page 16, "
+                        "pool 2048 pages, sm_scale 1, bf16 out"))
+
+    # ---- decode through the prefill entry, 64 requests, both families ----
+    if "decode_local_hd256" in want or "decode_global_hd512" in want:
+        kv = synth.uniform_lengths(64, 512, 8192, synth.generator(5))
+        for d, name in ((256, "decode_local_hd256"), (512, "decode_global_hd512")):
+            if name not in want:
+                continue
+            fam = synth.LOCAL if d == 256 else synth.GLOBAL
+            hkv = fam["num_kv_heads"]
+            gen = synth.generator(50 + d)
+            table = synth.random_page_table(kv, 16, 32768, gen)
+            numel = 32768 * 2 * hkv * 16 * d
+            pool = synth.normal_bf16((numel,), 0.25, synth.generator(500 + d, dev), device=dev)
+            q = synth.normal_bf16((64, 16, d), 0.25, gen).to(dev)
+            o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+            plan = plan_of(synth.lengths_to_indptr([1] * 64), table, 16, hkv, d, 32768)
+            pd = psw.pool_desc(pool, num_layers=1, num_pages=32768, page_size=16,
+                               num_kv_heads=hkv, head_dim=d)
+            wl = 1023 if d == 256 else -1
+            if d == 256:
+                def run(plan=plan, pd=pd, q=q, o=o):
+                    psw.paged_prefill_window_hd256(plan, pd, 0, q, 1.0, 1023, o)
+            else:
+                def run(plan=plan, pd=pd, q=q, o=o):
+                    psw.paged_prefill_hd512(plan, pd, 0, q, 1.0, o)
+            rows.append(Row(name, run, decode_bytes(kv, 16, hkv, d, wl), "GB/s", "hbm",
+                            f"decode (seq_len 1) hd{d}, 64 requests, KV ~ U[512, 8192], "
+                            f"{'window 1023' if wl >= 0 else 'full'}, 32768-page pool", hbm=True))
+    return rows
+
+
+def cpu_baseline(synth, oracle, case, budget_s=12.0):
+    """fp64 oracle on whole requests of the batch-8 windowed workload until the
+    time budget is spent; returns algorithmic TFLOP/s on that sample."""
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    g = oracle.PoolGeometry(1, case.num_pages, 8, 16, 256)
+    done, flops = [], 0.0
+    t0 = time.perf_counter()
+    order = np.argsort(case.qo_lens)       # shortest first so the sample stays bounded
+    for b in order:
+        oracle.paged_attention(case.q, case.pool, g, 0, case.qo_indptr,
+                               case.table.kv_page_indptr, case.table.kv_page_indices,
+                               case.table.kv_last_page_len, 1.0, 1023, requests=[int(b)])
+        done.append(int(b))
+        flops += attention_flops([case.qo_lens[b]], [case.kv_lens[b]], 16, 256, 1023)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    lens = [case.qo_lens[b] for b in done]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(done)} of 8 requests of the batch-8 windowed workload "
+                      f"(seq_len {lens}), all 16 heads, fp64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--rows", type=str, default="")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see the sharding note in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import paged_sliding_window_page_amd as psw
+
+    all_rows = ["prep_hd256", "prep_hd512", "prefill_window_hd256", "prefill_hd512",
+                "decode_local_hd256", "decode_global_hd512"]
+    want = set(args.rows.split(",")) if args.rows else set(all_rows)
+    dev = torch.device("cuda", 0)
+    log("building workloads ...")
+    rows = build_rows(torch, psw, synth, dev, want)
+    rows.sort(key=lambda r: all_rows.index(r.name))
+    flush = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+    torch.cuda.synchronize()
+    log("warmup ...")
+    for _ in range(args.warmup):
+        for r in rows:
+            r.run()
+    torch.cuda.synchronize()
+
+    evs = {r.name: [] for r in rows}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for r in rows:
+            if r.hbm:
+                flush.fill_(1)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            r.run()
+            e1.record()
+            evs[r.name].append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    out_rows = {}
+    for r in rows:
+        ms = np.array([a.elapsed_time(b) for a, b in evs[r.name]])
+        med = float(np.median(ms))
+        rate = r.work / (med * 1e-3) / (1e12 if r.unit == "TFLOP/s" else 1e9)
+        peak = PEAK_BF16_TFLOPS if r.unit == "TFLOP/s" else PEAK_HBM_GBS
+        out_rows[r.name] = {"achieved": round(rate, 3), "unit": r.unit, "peak": peak,
+                            "frac": round(rate / peak, 4), "bound": r.bound,
+                            "ms_median": round(med, 4), "ms_p10": round(float(np.percentile(ms, 10)), 4),
+                            "ms_p90": round(float(np.percentile(ms, 90)), 4),
+                            "work": r.work, "workload": r.desc}
+        log(f"{r.name:24s} {med * 1e3:9.1f} us  {rate:9.2f} {r.unit:8s} "
+            f"({100 * rate / peak:5.1f}% of peak)")
+
+    head = "prefill_window_hd256"
+    res = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded), random page tables",
+           "config": {"workload": "hd256 windowed paged prefill, batch 8, seq_len ~ U[128, 2048] "
+                                  "(seed 2), 16 Q / 8 KV heads, head_dim 256, page 16, "
+                                  "pool 4096 pages, window_left 1023, sm_scale 1",
+                      "rows": sorted(out_rows)},
+           "rows": out_rows}
+    if head in out_rows:
+        h = out_rows[head]
+        res["value"] = h["achieved"]
+        res["roofline"] = {"bound": "mfma", "achieved": h["achieved"], "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": h["frac"], "traffic": None,
+                           "kernel": "attention_kernel<256, false, true>",
+                           "algorithmic_flops_per_launch": h["work"]}
+        if not args.no_cpu:
+            import oracle
+            case = next(r for r in rows if r.name == head).case
+            log("timing the fp64 oracle on a bounded sample ...")
+            res["cpu_baseline"] = cpu_baseline(synth, oracle, case)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

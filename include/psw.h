@@ -1,0 +1,257 @@
+/*
+ * psw.h -- C ABI of the MI355X (gfx950) paged sliding-window attention library.
+ *
+ * Operations (all on one GPU, all on one ordered HIP stream):
+ *
+ *   paged_prefill_window_hd256          attention read through a page table,
+ *                                       head_dim 256, GQA, sliding window
+ *   paged_prefill_hd512                 the same at head_dim 512, full causal
+ *   qkv_norm_rope_paged_prefill_hd256   fused prep: Q norm+RoPE to a contiguous
+ *                                       buffer, K norm+RoPE and V weightless norm
+ *                                       scattered into the layer's pool pages
+ *   k_v_norm_rope_paged_prefill_hd512   fused prep: K norm+RoPE and V = weightless
+ *                                       norm of the same raw K (shared inv_rms)
+ *
+ * Sources (the pages this library implements):
+ *   [P1] PR "feat(kernels): Rust wrapper for the hd256 windowed paged prefill",
+ *        Description and Verification.
+ *   [P2] issue "gemma4: serving prep needs pool-write forms -- hd256 QKV in one
+ *        pass, hd512 V alongside K", Description, Proposed Plan, Acceptance
+ *        Criteria.
+ *   [P3] PR "feat(gemma4): paged KV serving across both attention families",
+ *        Description and the review thread (stream ordering, commit after
+ *        success).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Return value: PSW_OK (0) or a negative psw_status.  On any failure nothing
+ * has been launched and no device memory has been written; psw_last_error()
+ * returns a thread-local message naming the offending argument.  Every check
+ * runs on the host before any launch ([P1] Verification: contradictory layouts,
+ * out-of-range layers, page metadata past the pool, non-finite scales, lengths
+ * past i32 and zero KV heads all fail as errors before any launch).
+ *
+ * Pointers: "device" pointers are HIP device allocations owned by the caller
+ * (for example torch tensors); "host" pointers are read during the call only.
+ * The library never frees or retains caller memory.
+ *
+ * Pool layout (a whole-page, layer-indexed pool per KV family, bf16):
+ *     pool[layer][page][kv][kv_head][slot][dim]     kv = 0 for K, 1 for V
+ * i.e. numel == num_layers * num_pages * 2 * num_kv_heads * page_size * head_dim
+ * exactly; device offsets are 64-bit, so pools larger than 2 GiB are fine.
+ *
+ * Page table: CSR.  Request b owns kv_page_indices[kv_page_indptr[b] ..
+ * kv_page_indptr[b+1]) (at least one page) and its KV length is
+ * (n_pages - 1) * page_size + kv_last_page_len[b].  Its qo_len =
+ * qo_indptr[b+1] - qo_indptr[b] >= 1 queries are the last qo_len tokens of the
+ * KV: token t sits at position start_pos + t with start_pos = kv_len - qo_len
+ * ([P2] Proposed Plan: slot positions derive from start_pos + token).
+ *
+ * Ordering: a plan records the stream it was created with; every entry point
+ * rejects any other stream with PSW_E_PLAN, so pool initialisation, prep writes
+ * and attention reads stay ordered without events ([P3] review thread: a fresh
+ * stream on the same device races earlier KV writes).
+ */
+#ifndef PSW_H
+#define PSW_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t without including HIP headers (identical type). */
+typedef struct ihipStream_t* psw_stream_t;
+
+typedef enum {
+  PSW_OK = 0,
+  PSW_E_NULL = -1,      /* a required pointer is NULL                              */
+  PSW_E_SHAPE = -2,     /* malformed metadata: indptr not monotone, qo_len < 1,
+                           kv_len < qo_len, head_dim / page_size / batch invalid  */
+  PSW_E_RANGE = -3,     /* page id outside the pool, last_page_len outside
+                           [1, page_size], layer outside the pool, position past
+                           the RoPE table, window_left < -1, pages not covering   */
+  PSW_E_OVERFLOW = -4,  /* a length or total past INT32_MAX, or a size product
+                           that overflows int64                                   */
+  PSW_E_HEADS = -5,     /* zero KV heads, or query heads not a multiple of them    */
+  PSW_E_SCALE = -6,     /* non-finite sm_scale, or eps not finite and positive     */
+  PSW_E_PLAN = -7,      /* plan disagrees with the pool, the entry, its compiled
+                           tile, or the stream it was created on                  */
+  PSW_E_HIP = -8,       /* a HIP runtime call failed (message has the HIP error)   */
+  PSW_E_UNSUPPORTED = -9 /* a geometry this build has no kernel for               */
+} psw_status;
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* psw_last_error(void);
+
+/* Library version as a static string. */
+const char* psw_version(void);
+
+/* ---------------------------------------------------------------- pool ---- */
+
+/* A caller-owned bf16 pool in the layout above.  Geometry is re-derived with
+ * overflow-checked multiplies and must match numel exactly (whole pages). */
+typedef struct {
+  void* base;            /* device, bf16, numel elements                        */
+  int64_t numel;
+  int64_t num_layers;
+  int64_t num_pages;
+  int64_t page_size;     /* power of two, 1 .. 1024                             */
+  int64_t num_kv_heads;
+  int64_t head_dim;
+} psw_pool;
+
+/* Host-only check of a pool descriptor (the shared checked-geometry helper that
+ * both prep writes and attention reads go through, [P1] Description).  base may
+ * be NULL here; entry points additionally require it non-NULL. */
+int psw_check_pool(const psw_pool* pool);
+
+/* ---------------------------------------------------------------- plan ---- */
+
+/* Host description of one batch.  All arrays are HOST memory, int32, copied by
+ * psw_plan_create / psw_plan_update. */
+typedef struct {
+  int64_t batch;                    /* >= 1                                      */
+  const int32_t* qo_indptr;         /* [batch+1], [0] = 0, strictly increasing   */
+  const int32_t* kv_page_indptr;    /* [batch+1], [0] = 0, strictly increasing   */
+  const int32_t* kv_page_indices;   /* [kv_page_indptr[batch]]                   */
+  const int32_t* kv_last_page_len;  /* [batch], each in [1, page_size]           */
+  int64_t num_qo_heads;
+  int64_t num_kv_heads;             /* >= 1; num_qo_heads % num_kv_heads == 0    */
+  int64_t head_dim;
+  int64_t page_size;
+  int64_t num_pages;                /* pool size the page ids are checked against */
+  int64_t tile_q_override;          /* 0: derive tile_q; else the plan records
+                                       this value and prefill entries whose
+                                       compiled tile differs reject the plan     */
+} psw_plan_desc;
+
+/* Opaque plan: validated host copy of the metadata, the recorded bounds
+ * (max page id, max last-page length), the tile decision and work lists, and a
+ * device mirror uploaded lazily, on the plan's stream, by the first launch that
+ * needs it.  ([P1] Description: the plan records both bounds from its host
+ * inputs and settles the head relation before anything divides by it.) */
+typedef struct psw_plan psw_plan;
+
+/* Creates a plan bound to `stream`.  Pure host work: no HIP call is made here,
+ * so every reject can be exercised on a host without a GPU.  On failure *out is
+ * left untouched. */
+int psw_plan_create(const psw_plan_desc* desc, psw_stream_t stream, psw_plan** out);
+
+/* Replaces the plan's batch in place.  All or nothing: the new description is
+ * validated and the new state built completely before it is committed; on any
+ * failure the plan is unchanged ([P1] Description: bounds are committed only
+ * after an in-place update fully succeeds).  Head count, head_dim and
+ * page_size may change; the stream may not. */
+int psw_plan_update(psw_plan* plan, const psw_plan_desc* desc);
+
+/* Frees the plan and its device mirror (synchronises the plan's stream first
+ * if a mirror exists).  NULL is a no-op. */
+void psw_plan_destroy(psw_plan* plan);
+
+/* Read-only view of what a plan recorded. */
+typedef struct {
+  int64_t batch;
+  int64_t total_qo;          /* sum of qo_len                                    */
+  int64_t total_pages;       /* kv_page_indptr[batch]                            */
+  int64_t max_qo_len;
+  int64_t max_kv_len;
+  int64_t max_page_id;       /* recorded bound, checked against the pool         */
+  int64_t max_last_page_len; /* recorded bound, checked against page_size        */
+  int64_t num_qo_heads, num_kv_heads, head_dim, page_size, num_pages;
+  int64_t group;             /* num_qo_heads / num_kv_heads                      */
+  int64_t tile_q;            /* query tokens per prefill work-group              */
+  uint64_t generation;       /* bumped by every successful update                */
+  uint64_t digest;           /* FNV-1a over the recorded metadata                */
+} psw_plan_info;
+
+int psw_plan_get_info(const psw_plan* plan, psw_plan_info* info);
+
+/* Tile-size query ([P1] Description: the plan's recorded cta_tile_q is
+ * cross-checked against the kernel's own derivation).  Query tokens per prefill
+ * work-group for a GQA group and head_dim; positivity is checked in the i32
+ * domain. */
+int psw_prefill_tile_q(int64_t group, int64_t head_dim, int32_t* tile_q);
+
+/* ----------------------------------------------------------- attention ---- */
+
+/* Windowed paged prefill at head_dim 256 ([P1] Description).  Attention only:
+ * reads K/V of `layer` through the plan's page table, never writes the pool.
+ *   q:   device bf16 [total_qo][num_qo_heads][256], contiguous
+ *   o:   device [total_qo][num_qo_heads][256], fp32 (o_dtype 0) or bf16 (1)
+ *   sm_scale:    multiplies q.k before the softmax; must be finite (1.0 for the
+ *                unscaled attention the model runs)
+ *   window_left: key j is visible to the query at position p iff
+ *                0 <= p - j <= window_left (inclusive distance); -1 = no window
+ * qo_len == 1 for every request selects the split-KV decode kernels, otherwise
+ * the MFMA prefill kernel runs ([P3] Description: decode runs the prefill entry
+ * at one token). */
+int paged_prefill_window_hd256(psw_plan* plan, const psw_pool* pool, int64_t layer,
+                               const void* q, float sm_scale, int64_t window_left,
+                               void* o, int32_t o_dtype, psw_stream_t stream);
+
+/* Full causal paged prefill at head_dim 512 (the global family: 16 query heads
+ * over 1 KV head in the serving geometry), same contract without a window. */
+int paged_prefill_hd512(psw_plan* plan, const psw_pool* pool, int64_t layer,
+                        const void* q, float sm_scale, void* o, int32_t o_dtype,
+                        psw_stream_t stream);
+
+/* ----------------------------------------------------------------- prep ---- */
+
+/* hd256 fused prep ([P2] Proposed Plan), one pass per token:
+ *   q_out[t][h] = rope(rms(q_in[t][h]) * q_norm_w, p)           (contiguous)
+ *   K block     = rope(rms(k_in[t][g]) * k_norm_w, p)           (pool, layer)
+ *   V block     = v_in[t][g] * inv_rms(v_in[t][g])              (pool, layer)
+ * with rms(x) = x / sqrt(mean(x^2) + eps), p = start_pos + t, slot p in page
+ * ids[p / page_size].  RoPE rotates pairs (i, i + 128) by the angle whose cos
+ * and sin are rope_cos/rope_sin[p][i].  Math in fp32, one bf16 RNE store.
+ *   q_in: device bf16 [total_qo][num_qo_heads][256]; k_in, v_in: device bf16
+ *   [total_qo][num_kv_heads][256]; q_norm_w, k_norm_w: device bf16 [256];
+ *   rope_cos, rope_sin: device fp32 [rope_positions][128], with numel passed
+ *   for the length check; q_out: device bf16 [total_qo][num_qo_heads][256].
+ * Rejects: positions past rope_positions, table lengths that disagree, eps not
+ * finite and > 0, pages that do not cover [start_pos, start_pos + qo_len), and
+ * a page written by two requests. */
+int qkv_norm_rope_paged_prefill_hd256(psw_plan* plan, const psw_pool* pool, int64_t layer,
+                                      const void* q_in, const void* k_in, const void* v_in,
+                                      const void* q_norm_w, const void* k_norm_w,
+                                      const float* rope_cos, const float* rope_sin,
+                                      int64_t rope_positions, int64_t rope_cos_numel,
+                                      int64_t rope_sin_numel, float eps, void* q_out,
+                                      psw_stream_t stream);
+
+/* hd512 fused prep ([P2] Description and Proposed Plan): from the raw k_proj
+ * output alone,
+ *   inv     = 1 / sqrt(mean(k^2) + eps)
+ *   K block = rope(k * inv * k_norm_w, p)
+ *   V block = k * inv        (same inv, never rotated)
+ *   k_in: device bf16 [total_qo][num_kv_heads][512]; k_norm_w: device bf16 [512];
+ *   rope tables fp32 [rope_positions][256].  Same rejects as the hd256 prep. */
+int k_v_norm_rope_paged_prefill_hd512(psw_plan* plan, const psw_pool* pool, int64_t layer,
+                                      const void* k_in, const void* k_norm_w,
+                                      const float* rope_cos, const float* rope_sin,
+                                      int64_t rope_positions, int64_t rope_cos_numel,
+                                      int64_t rope_sin_numel, float eps,
+                                      psw_stream_t stream);
+
+/* RoPE tables for the prep entries: cos/sin[p][i] of p * theta^(-2i/head_dim),
+ * i < head_dim/2, p < positions, angles formed and evaluated in fp64 on the
+ * device, stored as fp32.  cos, sin: device fp32 [positions][head_dim/2]. */
+int psw_rope_tables(float* cos_out, float* sin_out, int64_t positions, int64_t head_dim,
+                    double theta, psw_stream_t stream);
+
+/* ----------------------------------------------------------- device check ---- */
+
+/* Second line of defence inside the prep kernels ([P2] Proposed Plan): a
+ * position past the RoPE table or a page id past the pool makes the kernel skip
+ * that row's writes and record the first offending value in a per-plan device
+ * word instead of trapping.  This call synchronises the plan's stream, returns
+ * 0 when nothing was recorded and PSW_E_RANGE otherwise (the word is cleared). */
+int psw_plan_device_errors(psw_plan* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PSW_H */

@@ -1,0 +1,274 @@
+"""Python binding of libpsw.so, the gfx950 paged sliding-window attention library.
+
+Argument marshalling only: every function here checks nothing of its own beyond
+what ctypes needs, passes device pointers and sizes to the C ABI declared in
+``include/psw.h`` and raises ``PswError`` with the library's message on a
+non-zero status.  All computation happens in the library's HIP kernels; there
+is no fallback.  Importing this package raises when ``libpsw.so`` has not been
+built (``python -m paged_sliding_window_page_amd.build``).
+
+Names follow the C ABI: ``paged_prefill_window_hd256``, ``paged_prefill_hd512``,
+``qkv_norm_rope_paged_prefill_hd256``, ``k_v_norm_rope_paged_prefill_hd512``,
+``rope_tables`` (``psw_rope_tables``), and the ``Plan`` object wrapping
+``psw_plan_*``.  Tensors are torch tensors on the current HIP device; the stream
+is torch's current stream unless one is passed.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpsw.so")
+
+PSW_OK = 0
+STATUS = {
+    0: "PSW_OK", -1: "PSW_E_NULL", -2: "PSW_E_SHAPE", -3: "PSW_E_RANGE", -4: "PSW_E_OVERFLOW",
+    -5: "PSW_E_HEADS", -6: "PSW_E_SCALE", -7: "PSW_E_PLAN", -8: "PSW_E_HIP",
+    -9: "PSW_E_UNSUPPORTED",
+}
+
+
+class PswError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+        self.status = STATUS.get(code, str(code))
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m paged_sliding_window_page_amd.build`")
+
+# The library takes torch's device pointers and streams, so it must run on the
+# same HIP runtime instance as torch.  torch ships its own libamdhip64 with the
+# same soname as the system one; importing torch first makes the dynamic loader
+# resolve libpsw.so's dependency to that already-loaded copy.
+import torch  # noqa: E402,F401
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+c_i64 = ctypes.c_int64
+c_i32 = ctypes.c_int32
+c_vp = ctypes.c_void_p
+c_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("base", c_vp), ("numel", c_i64), ("num_layers", c_i64), ("num_pages", c_i64),
+                ("page_size", c_i64), ("num_kv_heads", c_i64), ("head_dim", c_i64)]
+
+
+class PlanDesc(ctypes.Structure):
+    _fields_ = [("batch", c_i64), ("qo_indptr", c_i32p), ("kv_page_indptr", c_i32p),
+                ("kv_page_indices", c_i32p), ("kv_last_page_len", c_i32p),
+                ("num_qo_heads", c_i64), ("num_kv_heads", c_i64), ("head_dim", c_i64),
+                ("page_size", c_i64), ("num_pages", c_i64), ("tile_q_override", c_i64)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("batch", c_i64), ("total_qo", c_i64), ("total_pages", c_i64),
+                ("max_qo_len", c_i64), ("max_kv_len", c_i64), ("max_page_id", c_i64),
+                ("max_last_page_len", c_i64), ("num_qo_heads", c_i64), ("num_kv_heads", c_i64),
+                ("head_dim", c_i64), ("page_size", c_i64), ("num_pages", c_i64),
+                ("group", c_i64), ("tile_q", c_i64), ("generation", ctypes.c_uint64),
+                ("digest", ctypes.c_uint64)]
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_last_error = _sig("psw_last_error", ctypes.c_char_p)
+_version = _sig("psw_version", ctypes.c_char_p)
+_check_pool = _sig("psw_check_pool", ctypes.c_int, ctypes.POINTER(PoolDesc))
+_plan_create = _sig("psw_plan_create", ctypes.c_int, ctypes.POINTER(PlanDesc), c_vp,
+                    ctypes.POINTER(c_vp))
+_plan_update = _sig("psw_plan_update", ctypes.c_int, c_vp, ctypes.POINTER(PlanDesc))
+_plan_destroy = _sig("psw_plan_destroy", None, c_vp)
+_plan_info = _sig("psw_plan_get_info", ctypes.c_int, c_vp, ctypes.POINTER(PlanInfo))
+_tile_q = _sig("psw_prefill_tile_q", ctypes.c_int, c_i64, c_i64, c_i32p)
+_prefill256 = _sig("paged_prefill_window_hd256", ctypes.c_int, c_vp, ctypes.POINTER(PoolDesc),
+                   c_i64, c_vp, ctypes.c_float, c_i64, c_vp, c_i32, c_vp)
+_prefill512 = _sig("paged_prefill_hd512", ctypes.c_int, c_vp, ctypes.POINTER(PoolDesc), c_i64,
+                   c_vp, ctypes.c_float, c_vp, c_i32, c_vp)
+_prep256 = _sig("qkv_norm_rope_paged_prefill_hd256", ctypes.c_int, c_vp, ctypes.POINTER(PoolDesc),
+                c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
+                ctypes.c_float, c_vp, c_vp)
+_prep512 = _sig("k_v_norm_rope_paged_prefill_hd512", ctypes.c_int, c_vp, ctypes.POINTER(PoolDesc),
+                c_i64, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, ctypes.c_float, c_vp)
+_rope = _sig("psw_rope_tables", ctypes.c_int, c_vp, c_vp, c_i64, c_i64, ctypes.c_double, c_vp)
+_dev_err = _sig("psw_plan_device_errors", ctypes.c_int, c_vp)
+
+# every symbol include/psw.h declares
+EXPORTS = ["psw_last_error", "psw_version", "psw_check_pool", "psw_plan_create",
+           "psw_plan_update", "psw_plan_destroy", "psw_plan_get_info", "psw_prefill_tile_q",
+           "paged_prefill_window_hd256", "paged_prefill_hd512",
+           "qkv_norm_rope_paged_prefill_hd256", "k_v_norm_rope_paged_prefill_hd512",
+           "psw_rope_tables", "psw_plan_device_errors"]
+
+
+def _check(rc: int):
+    if rc != PSW_OK:
+        raise PswError(rc, _last_error().decode(errors="replace"))
+
+
+def version() -> str:
+    return _version().decode()
+
+
+def last_error() -> str:
+    return _last_error().decode(errors="replace")
+
+
+def _ptr(t):
+    """Device/host address of a tensor (or None / int passthrough)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def pool_desc(pool, *, num_layers, num_pages, page_size, num_kv_heads, head_dim,
+              numel=None) -> PoolDesc:
+    """Descriptor of a flat bf16 pool tensor (or a raw address with ``numel``)."""
+    if numel is None:
+        numel = pool.numel()
+    return PoolDesc(_ptr(pool), int(numel), int(num_layers), int(num_pages), int(page_size),
+                    int(num_kv_heads), int(head_dim))
+
+
+def check_pool(desc: PoolDesc) -> None:
+    _check(_check_pool(ctypes.byref(desc)))
+
+
+def prefill_tile_q(group: int, head_dim: int) -> int:
+    out = ctypes.c_int32(0)
+    _check(_tile_q(int(group), int(head_dim), ctypes.byref(out)))
+    return out.value
+
+
+def _i32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+class Plan:
+    """psw_plan: validated page-table metadata bound to one HIP stream."""
+
+    def __init__(self, qo_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len, *,
+                 num_qo_heads, num_kv_heads, head_dim, page_size, num_pages,
+                 tile_q_override=0, stream=None, batch=None):
+        self._h = c_vp()
+        self.stream = _stream_handle(stream) if stream != "none" else None
+        desc, keep = self._desc(qo_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len,
+                                num_qo_heads, num_kv_heads, head_dim, page_size, num_pages,
+                                tile_q_override, batch)
+        _check(_plan_create(ctypes.byref(desc), self.stream, ctypes.byref(self._h)))
+
+    @staticmethod
+    def _desc(qo_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
+              num_kv_heads, head_dim, page_size, num_pages, tile_q_override, batch):
+        arrs = [_i32(qo_indptr), _i32(kv_page_indptr), _i32(kv_page_indices),
+                _i32(kv_last_page_len)]
+        if batch is None:
+            batch = len(arrs[0]) - 1
+        ptrs = [a.ctypes.data_as(c_i32p) if a.size else ctypes.cast(None, c_i32p) for a in arrs]
+        desc = PlanDesc(int(batch), *ptrs, int(num_qo_heads), int(num_kv_heads), int(head_dim),
+                        int(page_size), int(num_pages), int(tile_q_override))
+        return desc, arrs
+
+    def update(self, qo_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len, *,
+               num_qo_heads, num_kv_heads, head_dim, page_size, num_pages, tile_q_override=0,
+               batch=None):
+        desc, keep = self._desc(qo_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len,
+                                num_qo_heads, num_kv_heads, head_dim, page_size, num_pages,
+                                tile_q_override, batch)
+        _check(_plan_update(self._h, ctypes.byref(desc)))
+
+    def info(self) -> dict:
+        out = PlanInfo()
+        _check(_plan_info(self._h, ctypes.byref(out)))
+        return {f: getattr(out, f) for f, _ in PlanInfo._fields_}
+
+    def device_errors(self) -> None:
+        _check(_dev_err(self._h))
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if self._h:
+            _plan_destroy(self._h)
+            self._h = c_vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def paged_prefill_window_hd256(plan: Plan, pool: PoolDesc, layer: int, q, sm_scale: float,
+                               window_left: int, o, stream=None) -> None:
+    """o <- windowed paged attention of q over ``layer`` of the pool (o fp32 or bf16)."""
+    import torch
+    o_dtype = 1 if o.dtype == torch.bfloat16 else 0
+    _check(_prefill256(plan.handle, ctypes.byref(pool), int(layer), _ptr(q), float(sm_scale),
+                       int(window_left), _ptr(o), o_dtype,
+                       plan.stream if stream is None else _stream_handle(stream)))
+
+
+def paged_prefill_hd512(plan: Plan, pool: PoolDesc, layer: int, q, sm_scale: float, o,
+                        stream=None) -> None:
+    """o <- full causal paged attention at head_dim 512."""
+    import torch
+    o_dtype = 1 if o.dtype == torch.bfloat16 else 0
+    _check(_prefill512(plan.handle, ctypes.byref(pool), int(layer), _ptr(q), float(sm_scale),
+                       _ptr(o), o_dtype,
+                       plan.stream if stream is None else _stream_handle(stream)))
+
+
+def qkv_norm_rope_paged_prefill_hd256(plan: Plan, pool: PoolDesc, layer: int, q_in, k_in, v_in,
+                                      q_norm_w, k_norm_w, rope_cos, rope_sin, eps: float, q_out,
+                                      rope_positions=None, stream=None) -> None:
+    if rope_positions is None:
+        rope_positions = rope_cos.shape[0]
+    _check(_prep256(plan.handle, ctypes.byref(pool), int(layer), _ptr(q_in), _ptr(k_in),
+                    _ptr(v_in), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(rope_cos), _ptr(rope_sin),
+                    int(rope_positions), int(rope_cos.numel()), int(rope_sin.numel()),
+                    float(eps), _ptr(q_out),
+                    plan.stream if stream is None else _stream_handle(stream)))
+
+
+def k_v_norm_rope_paged_prefill_hd512(plan: Plan, pool: PoolDesc, layer: int, k_in, k_norm_w,
+                                      rope_cos, rope_sin, eps: float, rope_positions=None,
+                                      stream=None) -> None:
+    if rope_positions is None:
+        rope_positions = rope_cos.shape[0]
+    _check(_prep512(plan.handle, ctypes.byref(pool), int(layer), _ptr(k_in), _ptr(k_norm_w),
+                    _ptr(rope_cos), _ptr(rope_sin), int(rope_positions), int(rope_cos.numel()),
+                    int(rope_sin.numel()), float(eps),
+                    plan.stream if stream is None else _stream_handle(stream)))
+
+
+def rope_tables(cos_out, sin_out, positions: int, head_dim: int, theta: float,
+                stream=None) -> None:
+    """Fill fp32 [positions][head_dim/2] cos/sin tables on the device."""
+    _check(_rope(_ptr(cos_out), _ptr(sin_out), int(positions), int(head_dim), float(theta),
+                 _stream_handle(stream)))

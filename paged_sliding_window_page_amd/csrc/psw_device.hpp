@@ -1,0 +1,96 @@
+// Device-side types, pool addressing and launcher declarations shared by the
+// HIP translation units of the library (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace psw_dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Pool addressing (element strides, 64-bit).  Per layer and page there is a K
+// block [kv_head][slot][dim] followed by a V block stored dim-major,
+// [kv_head][dim][slot]: V is the operand contracted over keys, so keeping keys
+// contiguous lets the attention kernels fetch it with the same 16-byte loads as
+// K, without a transpose anywhere on the read path.
+struct PoolStrides {
+  int64_t layer;      // num_pages * 2 * H_kv * P * D
+  int64_t page;       // 2 * H_kv * P * D
+  int64_t kv;         // H_kv * P * D   (K block -> V block)
+  int64_t head;       // P * D
+  int32_t page_shift; // log2(P)
+  int32_t page_size;
+};
+
+// Work item of the attention kernels: (request, first query token, first key,
+// last key inclusive).  In split-KV mode the item index is the partial slot.
+struct AttnParams {
+  const __bf16* q;
+  void* o;
+  float* part_o;       // split mode: [n_partials][H_q][D] unnormalised
+  float* part_ml;      // split mode: [n_partials][H_q][2] (running max in log2 units, sum)
+  const __bf16* pool;
+  const int32_t* qo_indptr;
+  const int32_t* kv_page_indptr;
+  const int32_t* kv_page_indices;
+  const int32_t* kv_len;
+  const int32_t* items;
+  PoolStrides ps;
+  int64_t layer_off;
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t group_shift;  // log2(H_q / H_kv)
+  int32_t window_left;  // -1: none
+  float scale_log2;     // sm_scale * log2(e)
+};
+
+struct MergeParams {
+  const float* part_o;
+  const float* part_ml;
+  const int32_t* req_splits;  // pairs (first slot, count)
+  const int32_t* qo_indptr;
+  void* o;
+  int32_t num_qo_heads;
+};
+
+// Prep work item: (request, first global token, tokens (<= 16), page id,
+// first slot, first position).  Every item lies inside one page.
+struct PrepParams {
+  const __bf16* q_in;
+  const __bf16* k_in;
+  const __bf16* v_in;
+  const __bf16* q_w;
+  const __bf16* k_w;
+  const float* cos;
+  const float* sin;
+  __bf16* q_out;
+  __bf16* pool;
+  int32_t* err;
+  const int32_t* items;
+  PoolStrides ps;
+  int64_t layer_off;
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t num_pages;
+  int32_t rope_positions;
+  float eps;
+};
+
+constexpr int kPrepItemInts = 6;
+constexpr int kPrepMaxTokens = 16;
+
+// Launchers (return the hipError_t of the launch).
+hipError_t launch_attention(int head_dim, bool split, bool out_bf16, const AttnParams& p,
+                            int n_items, hipStream_t s);
+hipError_t launch_merge(int head_dim, bool out_bf16, const MergeParams& p, int batch,
+                        hipStream_t s);
+hipError_t launch_prep_hd256(const PrepParams& p, int n_items, hipStream_t s);
+hipError_t launch_prep_hd512(const PrepParams& p, int n_items, hipStream_t s);
+hipError_t launch_rope_tables(float* c, float* s, int64_t positions, int64_t half, double theta,
+                              hipStream_t st);
+
+}  // namespace psw_dev

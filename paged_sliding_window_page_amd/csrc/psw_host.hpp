@@ -1,0 +1,125 @@
+// Internal host-side declarations: validation, the plan and its schedules.
+// This header and psw_host.cpp use no HIP API, so every host check can be
+// exercised on a machine without a GPU.  Sources:
+//   [P1] PR "feat(kernels): Rust wrapper for the hd256 windowed paged prefill",
+//        Description, Verification.
+//   [P2] issue "gemma4: serving prep needs pool-write forms -- hd256 QKV in one
+//        pass, hd512 V alongside K", Proposed Plan.
+//   [P3] PR "feat(gemma4): paged KV serving across both attention families",
+//        Description and review thread.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "psw.h"
+
+namespace psw {
+
+// ----------------------------------------------------------------- errors --
+
+// Records a thread-local message and returns `code` (for `return fail(...)`).
+int fail(int code, const std::string& msg);
+void clear_error();
+
+// Checked narrowing to int32 ([P1] Description: scalar narrowing goes through
+// checked conversions so a length past i32 fails instead of truncating).
+bool fits_i32(int64_t v);
+// a * b without int64 overflow; false on overflow or negative operands.
+bool checked_mul(int64_t a, int64_t b, int64_t* out);
+
+// ------------------------------------------------------------------- pool --
+
+int check_pool(const psw_pool* pool, bool need_base);
+
+// ------------------------------------------------------------------- plan --
+
+// Tiling decisions, shared by the plan (which records them) and the device
+// code (which was compiled for them).
+constexpr int kPrefillRows = 128;          // query rows (token x head) per work-group
+constexpr int kKvTile256 = 64;             // keys per prefill tile at head_dim 256
+constexpr int kKvTile512 = 32;             // keys per prefill tile at head_dim 512
+constexpr int kDecodeKeysPerSubtile = 32;  // keys one decode wave handles per step
+constexpr int kMaxGroup = 32;
+
+int derive_tile_q(int64_t group, int64_t head_dim, int32_t* tile_q);
+inline int kv_tile_for(int64_t head_dim) { return head_dim == 512 ? kKvTile512 : kKvTile256; }
+
+struct PlanState {
+  int32_t batch = 0;
+  int32_t num_qo_heads = 0, num_kv_heads = 0, head_dim = 0, page_size = 0, num_pages = 0;
+  int32_t group = 0;
+  int32_t tile_q = 0;
+  bool tile_overridden = false;
+  int32_t total_qo = 0, total_pages = 0;
+  int32_t max_qo_len = 0, max_kv_len = 0;
+  int32_t max_page_id = -1, max_last_page_len = 0;
+  std::vector<int32_t> qo_indptr, kv_page_indptr, kv_page_indices, last_page_len, kv_len;
+  uint64_t digest = 0;
+};
+
+// Builds and validates a complete PlanState from a description; *out is only
+// written on success.
+int build_state(const psw_plan_desc* d, PlanState* out);
+
+// Attention work item: quads (request, first query token, first key, last key
+// inclusive).  Prefill: one item per (request, query tile), heaviest first.
+struct PrefillSchedule {
+  int64_t window_left = -2;   // key the schedule was built for (-2 = none)
+  int32_t kv_tile = 0;
+  int32_t tile_q = 0;
+  std::vector<int32_t> items;  // quads
+  int64_t total_tiles = 0;     // sum over items of KV tiles visited
+};
+void build_prefill_schedule(const PlanState& st, int64_t window_left, int32_t kv_tile,
+                            PrefillSchedule* out);
+
+// Decode (qo_len == 1 everywhere) split-KV schedule.  Items are quads like the
+// prefill ones (request, 0, first key, last key); item i writes partial slot i.
+struct DecodeSchedule {
+  int64_t window_left = -2;
+  int32_t chunk = 0;                 // keys per split
+  std::vector<int32_t> items;        // quads
+  std::vector<int32_t> req_splits;   // pairs (first partial slot, number of splits) per request
+  int32_t num_partials = 0;
+};
+void build_decode_schedule(const PlanState& st, int64_t window_left, int32_t kv_tile,
+                           DecodeSchedule* out);
+
+// Prep work items: up to 16 consecutive positions of one request inside one
+// page, as (request, first global token, tokens, page id, first slot, first
+// position).
+void build_prep_items(const PlanState& st, std::vector<int32_t>* out);
+
+// Window normalisation: -1 when the window cannot exclude any key.
+int64_t effective_window(const PlanState& st, int64_t window_left);
+
+// Checks shared by the attention entries before any HIP call.
+int check_attention_call(const psw_plan* plan, const psw_pool* pool, int64_t layer,
+                         const void* q, float sm_scale, int64_t window_left, const void* o,
+                         int32_t o_dtype, psw_stream_t stream, int64_t want_head_dim);
+
+// Checks shared by the prep entries before any HIP call.
+int check_prep_call(const psw_plan* plan, const psw_pool* pool, int64_t layer,
+                    int64_t want_head_dim, const float* rope_cos, const float* rope_sin,
+                    int64_t rope_positions, int64_t rope_cos_numel, int64_t rope_sin_numel,
+                    float eps, psw_stream_t stream);
+
+}  // namespace psw
+
+// Device mirror (defined in the HIP translation unit; opaque here).
+struct psw_device_mirror;
+psw_device_mirror* psw_mirror_new();
+void psw_mirror_free(psw_device_mirror* m);
+
+struct psw_plan {
+  psw_stream_t stream = nullptr;
+  psw::PlanState st;
+  uint64_t generation = 0;
+  psw::PrefillSchedule prefill;
+  psw::DecodeSchedule decode;
+  std::vector<int32_t> prep_items;
+  bool prep_built = false;
+  psw_device_mirror* mirror = nullptr;  // created by the first launch
+};
