@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpsw.so")
 
-SOURCES = ["psw_host.cpp", "psw_entry.hip", "psw_attention.hip", "psw_prep.hip"]
+SOURCES = ["psw_host.cpp", "psw_entry.hip", "psw_attn256.hip", "psw_attn512.hip", "psw_prep.hip"]
 
 
 def _hipcc() -> str:
@@ -41,9 +41,17 @@ def _flags():
     ]
 
 
+# Per-file code-generation options.  The head_dim-256 attention kernels keep
+# their MFMA accumulators (O and S) in VGPRs so the softmax and the rare O
+# rescale touch them without AGPR round trips; Q fragments then go to AGPRs,
+# which the MFMA reads directly.  (At head_dim 512, O alone fills 256
+# registers, so it stays in AGPRs.)
+EXTRA = {"psw_attn256.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *_flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         # host-only translation unit: no device code
         cmd = [_hipcc(), "-O2", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",

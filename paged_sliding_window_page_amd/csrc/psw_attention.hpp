@@ -1,0 +1,456 @@
+// Paged prefill attention for gfx950: bf16 MFMA, online softmax, K/V gathered
+// through a page table.  One kernel template serves
+//   * windowed paged prefill at head_dim 256 (PR "feat(kernels): Rust wrapper
+//     for the hd256 windowed paged prefill", Description: explicit sm_scale,
+//     window_left an inclusive distance, addresses from page ids and the
+//     last-page length),
+//   * full paged prefill at head_dim 512 (PR "feat(gemma4): paged KV serving
+//     across both attention families", Description: global layers are full
+//     attention at head_dim 512 with one KV head),
+//   * the split-KV form that one-token decode runs through the same entry
+//     (same PR, Description: decode runs the prefill entry at seq_len 1), whose
+//     partial results are combined by merge_kernel.
+//
+// Work-group: 4 waves, 128 query rows = (128 / group) tokens x group heads of
+// one KV head, so the group's heads share every K/V tile.  Each wave owns 32
+// rows.  Per KV tile (64 keys at D=256, 32 at D=512):
+//   S^T[key][row] = K Q^T     v_mfma_f32_32x32x16_bf16, K from LDS (A), Q in
+//                             registers (B)
+//   P = exp2(S*scale*log2e - m) with a lazily raised running max m
+//   O^T[d][row]  += V^T P^T   V^T from LDS (A), P^T straight from the S^T
+//                             accumulators (B), O^T in accumulator registers
+// The K rows feeding S^T are read in a permuted order (kperm below) chosen so
+// that the keys a lane holds in its S^T accumulators are exactly the 8
+// consecutive keys its P^T operand needs; no data moves between the two MFMAs.
+//
+// Tiles are fetched with global_load_lds_dwordx4 (16 B per lane straight into
+// LDS, no VGPR staging) into a double buffer; the next tile's loads are in
+// flight while the current one is multiplied.  LDS tiles are XOR-swizzled so
+// that the MFMA operand reads (ds_read_b128) hit distinct banks.  Only tiles
+// that intersect a row's window are visited; whole tiles inside every row's
+// window skip the element mask.
+#pragma once
+#include "psw_device.hpp"
+
+namespace psw_dev {
+namespace {
+
+constexpr float kNegBig = -1.0e30f;     // finite "minus infinity" for running maxima
+constexpr float kRescaleSlack = 8.0f;   // log2 units: rescale O only past a 256x rise
+
+__device__ __forceinline__ int kperm(int m) {
+  // S^T row m (0..31) -> key within the 32-key block.  With the 32x32 MFMA
+  // accumulator layout (lane half h, register r holds row 8*(r/4) + 4*h + r%4)
+  // this puts key 16*(r/8) + 8*h + (r%8) in register r of half h.
+  return ((m >> 4) << 4) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2) | (m & 3);
+}
+
+// XOR swizzle of the 16-byte chunk index inside a K row (bank spread).
+__device__ __forceinline__ int kswz(int key) {
+  return (key & 3) | ((key >> 1) & 4) | ((key << 1) & 8);
+}
+
+__device__ __forceinline__ void lds_load16(const void* gsrc, void* ldst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (__attribute__((address_space(3))) void*)ldst, 16, 0, 0);
+}
+
+// Wave-uniform read of read-only metadata through the scalar data cache
+// (constant address space), so it never waits behind vector memory traffic.
+template <typename T>
+__device__ __forceinline__ T ldu(const T* p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) T*>(
+      reinterpret_cast<const __attribute__((address_space(4))) char*>(
+          (const __attribute__((address_space(4))) char*)p));
+}
+
+// Keep the compiler from if-converting a rare branch into straight-line code.
+__device__ __forceinline__ void rare_path() { asm volatile("" ::: "memory"); }
+
+template <int D, bool SPLIT, bool OUT_BF16>
+__global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
+  constexpr int KT = D == 256 ? 64 : 32;  // keys per tile
+  constexpr int NCH = D / 8;              // 16-B chunks per K row
+  constexpr int KBLK = KT / 32;           // S^T 32-key blocks per tile
+  constexpr int NT = KT / 16;             // PV steps (16 keys each) per tile
+  constexpr int DB = D / 32;              // O^T 32-row blocks
+  constexpr int KS = D / 16;              // QK k-steps
+  constexpr int TILE = KT * D * 2;        // bytes of one K (or V^T) tile: 32 KiB
+  constexpr int ROUNDS = TILE / (256 * 16);
+  constexpr int KEYS_PER_LOAD = 1024 / (D * 2);  // keys one K load instruction covers
+
+  // K and V^T tiles have separate double buffers: K[t+1] must be resident
+  // while V[t-1] is still being read (see the pipeline below).
+  __shared__ __attribute__((aligned(1024))) char ks_lds[2][TILE];
+  __shared__ __attribute__((aligned(1024))) char vs_lds[2][TILE];
+
+  const int lane = threadIdx.x & 63;
+  // wave index, explicitly wave-uniform so that per-wave address math is scalar
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int hkv = P.num_kv_heads;
+  const int item = blockIdx.x / hkv;
+  const int kvh = blockIdx.x - item * hkv;
+  const int b = ldu(P.items + 4 * item + 0);
+  const int t0 = ldu(P.items + 4 * item + 1);
+  const int k_lo = ldu(P.items + 4 * item + 2);
+  const int k_hi = ldu(P.items + 4 * item + 3);
+  const int q_beg = ldu(P.qo_indptr + b);
+  const int qo_len = ldu(P.qo_indptr + b + 1) - q_beg;
+  const int kvl = ldu(P.kv_len + b);
+  const int start = kvl - qo_len;
+  const int pg0 = ldu(P.kv_page_indptr + b);
+  const int32_t* pages = P.kv_page_indices + pg0;
+  const int last_page = ldu(P.kv_page_indptr + b + 1) - pg0 - 1;
+  const int gs = P.group_shift;
+  const int tok_w = 32 >> gs;            // tokens per wave
+  const int wl = P.window_left;
+
+  // this lane's query row: token t0 + tl, head kvh*group + hh
+  const int tl = w * tok_w + (n >> gs);
+  const int hh = n & ((1 << gs) - 1);
+  const int tok = t0 + tl;
+  const bool row_valid = tok < qo_len;
+  const int pos = start + tok;
+  const int head = (kvh << gs) + hh;
+  // keys this lane's row may see: [lo_n, hi_n] (empty for padding rows)
+  const int hi_n = row_valid ? min(k_hi, pos) : -1;
+  const int lo_n = max(k_lo, wl >= 0 ? pos - wl : 0);
+  // the same range, over every row of this wave (for whole-tile decisions)
+  const int wt0 = t0 + w * tok_w;
+  const int w_pmin = start + wt0;
+  const int w_pmax = start + min(wt0 + tok_w, qo_len) - 1;
+  const bool wave_live = wt0 < qo_len;
+
+  bf16x8 qf[KS];
+  {
+    const __bf16* qrow = P.q + ((int64_t)(q_beg + (row_valid ? tok : 0)) * P.num_qo_heads + head) * D + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
+      qf[ks] = row_valid ? v : bf16x8{};
+    }
+  }
+
+  const char* kbase_g = reinterpret_cast<const char*>(P.pool + P.layer_off + (int64_t)kvh * P.ps.head);
+  const char* vbase_g = kbase_g + P.ps.kv * 2;
+  const int pshift = P.ps.page_shift;
+  const int psize = P.ps.page_size;
+  const int64_t page_bytes = P.ps.page * 2;
+
+  const int jt0 = k_lo / KT;
+  const int jt1 = k_hi / KT;
+  const int ntiles = jt1 - jt0 + 1;
+
+  // ---- tile loads: every load instruction reads from one page ----
+  // K tile in LDS: [key][chunk ^ kswz(key)] of 16-byte chunks (D/8 per key).
+  // V^T tile in LDS: [k8][d] of 16-byte chunks, chunk (k8, d) holding the 8
+  // keys 8*k8 .. 8*k8+7 of dim d.  Eight lanes reading consecutive d at one k8
+  // touch consecutive 16-byte chunks, so no swizzle is needed.
+  // Load instruction r of wave w covers K keys (r*4+w)*KEYS_PER_LOAD.. and the
+  // V^T chunks k8 = (r*4+w)*64 / D, d = ((r*4+w)*64) % D + lane: one page each.
+  int koff[ROUNDS], voff[ROUNDS];   // per-lane byte offsets inside the page
+  int kpg[ROUNDS], vpg[ROUNDS];     // page of the tile (wave-uniform)
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int ins = r * 4 + w;
+    const int u = ins * 64 + lane;
+    const int key = u / NCH;
+    const int c = (u % NCH) ^ kswz(key);
+    kpg[r] = (ins * KEYS_PER_LOAD) >> pshift;
+    koff[r] = (key & (psize - 1)) * D * 2 + c * 16;
+    const int k8 = (ins * 64) / D;
+    const int d = (ins * 64) % D + lane;
+    vpg[r] = (8 * k8) >> pshift;
+    voff[r] = d * psize * 2 + ((8 * k8) & (psize - 1)) * 2;
+  }
+  // page pointers of tile j0: pages are clamped to the request's last page
+  // (keys past kv_len are masked, and their V values zeroed after landing)
+  auto page_ptr = [&](const char* base, int j0, int p) {
+    const int idx = min((j0 >> pshift) + p, last_page);
+    return base + (int64_t)ldu(pages + idx) * page_bytes;
+  };
+  auto issue_k = [&](int st, int j0) {
+    char* kl = ks_lds[st];
+    const int slot0 = KT < psize ? (j0 & (psize - 1)) * D * 2 : 0;
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r)
+      lds_load16(page_ptr(kbase_g, j0, kpg[r]) + slot0 + koff[r], kl + (r * 4 + w) * 1024);
+  };
+  auto issue_v = [&](int st, int j0) {
+    char* vl = vs_lds[st];
+    const int slot0 = KT < psize ? (j0 & (psize - 1)) * 2 : 0;
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r)
+      lds_load16(page_ptr(vbase_g, j0, vpg[r]) + slot0 + voff[r], vl + (r * 4 + w) * 1024);
+  };
+  // Zero, in the V^T chunks this lane loaded itself, the keys at or past
+  // kv_len (their pool slots may hold anything, NaN included, and 0 * NaN would
+  // leak into O).  Called after this wave's loads have landed.
+  auto sanitize = [&](int st, int j0) {
+    if (j0 + KT <= kvl) return;
+    rare_path();
+    char* vl = vs_lds[st];
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      const int jc = j0 + 8 * (((r * 4 + w) * 64) / D);
+      if (jc + 8 > kvl) {
+        bf16x8* cp = reinterpret_cast<bf16x8*>(vl + (r * 4 + w) * 1024 + lane * 16);
+        bf16x8 v = *cp;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (jc + e >= kvl) ? (__bf16)0.0f : v[e];
+        *cp = v;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- per-lane LDS operand addresses ----
+  // K row of S^T row n in block kb: key 32*kb + kperm(n); its 16-B chunk 2*ks+h
+  // sits at position (2*ks+h) ^ kswz(key).  Writing sw = kswz(key), that is
+  // 2*(ks ^ (sw>>1)) + (h ^ (sw&1)) for ks < 8, so the byte offset is
+  // kaddr0 ^ (ks << 5), plus 256 for every further 8 k-steps.
+  const int krow = kperm(n);
+  const int ksw = kswz(krow);
+  const int kaddr0 = krow * NCH * 16 + 16 * (h ^ (ksw & 1)) + 32 * (ksw >> 1);
+  // V^T operand of PV step t, O^T block db: row d = 32*db + n, keys
+  // 16t + 8h .. +7, i.e. chunk (k8 = 2t + h, d).
+  const int vaddr0 = (h * D + n) * 16;
+  auto vaddr = [&](int t, int db) { return vaddr0 + (2 * t * D + 32 * db) * 16; };
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+  float m_run = kNegBig;
+  float l_run = 0.0f;
+  bf16x8 pprev[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) pprev[t] = bf16x8{};
+  // scores enter the softmax as s * sm_scale * log2(e); the running max is
+  // kept in those units.  A negative scale flips which raw score is largest.
+  const float c2 = P.scale_log2;
+
+  // S^T for one tile.  K operands are read two k-steps ahead; the scheduling
+  // barrier keeps the compiler from hoisting every read.
+  auto qk = [&](int st, f32x16* s) {
+    const char* kl = ks_lds[st];
+    bf16x8 a[3][KBLK];
+    auto ld = [&](int ks, bf16x8* dst) {
+#pragma unroll
+      for (int kb = 0; kb < KBLK; ++kb)
+        dst[kb] = *reinterpret_cast<const bf16x8*>(
+            kl + (kaddr0 ^ ((ks & 7) << 5)) + (ks >> 3) * 256 + kb * 32 * NCH * 16);
+    };
+#pragma unroll
+    for (int kb = 0; kb < KBLK; ++kb) s[kb] = f32x16{};
+    ld(0, a[0]);
+    ld(1, a[1]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 2 < KS) ld(ks + 2, a[(ks + 2) % 3]);
+#pragma unroll
+      for (int kb = 0; kb < KBLK; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks % 3][kb], qf[ks], s[kb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // O^T += V^T P^T for one tile (V^T operands read two steps ahead).
+  auto pv = [&](int st, const bf16x8* pb) {
+    const char* vl = vs_lds[st];
+    constexpr int NSTEP = NT * DB;
+    bf16x8 a[3];
+    auto ld = [&](int i) { return *reinterpret_cast<const bf16x8*>(vl + vaddr(i / DB, i % DB)); };
+    a[0] = ld(0);
+    a[1] = ld(1);
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) {
+      if (i + 2 < NSTEP) a[(i + 2) % 3] = ld(i + 2);
+      oacc[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % 3], pb[i / DB], oacc[i % DB],
+                                                              0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Row max of raw scores in softmax units, with or without the element mask.
+  // Register r of block kb holds key j0 + 32*kb + 16*(r/8) + 8*h + r%8.
+  auto tile_max = [&](f32x16* s, bool masked, int j0) {
+    float mx = -__builtin_inff();
+    if (!masked) {
+      float hi = -__builtin_inff(), lo = __builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          hi = fmaxf(hi, s[kb][r]);
+          lo = fminf(lo, s[kb][r]);
+        }
+      mx = c2 >= 0.0f ? hi * c2 : lo * c2;
+    } else {
+      rare_path();
+      const int kb0 = j0 + 8 * h - lo_n;
+      const unsigned span = (unsigned)(hi_n - lo_n);
+#pragma unroll
+      for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const unsigned rel = (unsigned)(kb0 + 32 * kb + 16 * (r >> 3) + (r & 7));
+          const float v = rel <= span ? s[kb][r] * c2 : -__builtin_inff();
+          s[kb][r] = v;   // masked tiles keep scaled scores
+          mx = fmaxf(mx, v);
+        }
+    }
+    return fmaxf(mx, __shfl_xor(mx, 32));
+  };
+
+  // ---- prologue: K[0], V[0] (and K[1]) resident ----
+  issue_k(0, jt0 * KT);
+  issue_v(0, jt0 * KT);
+  if (ntiles > 1) issue_k(1, (jt0 + 1) * KT);
+  __builtin_amdgcn_s_waitcnt(0);
+  sanitize(0, jt0 * KT);
+  __syncthreads();
+
+  // Pipeline, iteration t (K[t] and V[t-1] resident, V[t] / K[t+1] landed or
+  // in flight):  S = Q K[t]^T;  softmax of tile t;  O += P[t-1] V[t-1];
+  // rescale O if the running max rose;  then make V[t], K[t+1] resident and
+  // start V[t+1], K[t+2].
+  for (int it = 0; it < ntiles; ++it) {
+    const int st = it & 1;
+    const int j0 = (jt0 + it) * KT;
+    bf16x8 pcur[NT];
+    float lsum = 0.0f;
+    float m_new;
+    bool need;
+    {
+      f32x16 s[KBLK];
+      qk(st, s);
+      // A tile inside every row's range of this wave needs no element mask;
+      // a tile outside every row's range is fully masked.
+      const bool full = wave_live && j0 >= k_lo && j0 + KT - 1 <= k_hi && j0 + KT - 1 <= w_pmin &&
+                        (wl < 0 || w_pmax - j0 <= wl);
+      const float tmax = tile_max(s, !full, j0);
+      m_new = fmaxf(m_run, tmax);
+      need = __any(m_new > m_run + kRescaleSlack);
+      const float m_use = need ? m_new : m_run;
+      if (full) {
+#pragma unroll
+        for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c2, -m_use));
+            s[kb][r] = p;
+            lsum += p;
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(s[kb][r] - m_use);
+            s[kb][r] = p;
+            lsum += p;
+          }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pcur[t][i] = (__bf16)s[t >> 1][8 * (t & 1) + i];
+      pv(st ^ 1, pprev);
+    }
+    if (need) {
+      rare_path();
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+    }
+    l_run += lsum;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) pprev[t] = pcur[t];
+
+    // make V[t] and K[t+1] resident; the buffers of K[t] and V[t-1] are free
+    // once every wave is past this barrier
+    __builtin_amdgcn_s_waitcnt(0);
+    if (it >= 1) sanitize(st, j0);
+    __syncthreads();
+    if (it + 1 < ntiles) {
+      issue_v(st ^ 1, j0 + KT);
+      if (it + 2 < ntiles) issue_k(st, j0 + 2 * KT);
+    }
+  }
+  pv((ntiles - 1) & 1, pprev);
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!row_valid) return;
+  // lane (n, h), O^T block db, register r holds d = 32*db + 8*(r/4) + 4*h + r%4
+  if constexpr (SPLIT) {
+    const int64_t base = ((int64_t)item * P.num_qo_heads + head);
+    float* po = P.part_o + base * D + 4 * h;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+        *reinterpret_cast<f32x4*>(po + 32 * db + 8 * g) = v;
+      }
+    if (h == 0) {
+      P.part_ml[base * 2 + 0] = m_run;
+      P.part_ml[base * 2 + 1] = l_tot;
+    }
+  } else {
+    const float inv = 1.0f / l_tot;
+    const int64_t orow = ((int64_t)(q_beg + tok) * P.num_qo_heads + head) * D + 4 * h;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int off = 32 * db + 8 * g;
+        if constexpr (OUT_BF16) {
+          bf16x4 v = {(__bf16)(oacc[db][4 * g] * inv), (__bf16)(oacc[db][4 * g + 1] * inv),
+                      (__bf16)(oacc[db][4 * g + 2] * inv), (__bf16)(oacc[db][4 * g + 3] * inv)};
+          *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(P.o) + orow + off) = v;
+        } else {
+          f32x4 v = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
+                     oacc[db][4 * g + 3] * inv};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(P.o) + orow + off) = v;
+        }
+      }
+  }
+}
+
+// Combines the split-KV partials of one (request, head): with per-split running
+// max m_s (log2 units), sum l_s and unnormalised o_s,
+//   O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,   M = max_s m_s.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(D / 4) void merge_kernel(MergeParams P) {
+  const int b = blockIdx.x / P.num_qo_heads;
+  const int head = blockIdx.x - b * P.num_qo_heads;
+  const int first = P.req_splits[2 * b];
+  const int ns = P.req_splits[2 * b + 1];
+  float M = kNegBig;
+  for (int s = 0; s < ns; ++s)
+    M = fmaxf(M, P.part_ml[((int64_t)(first + s) * P.num_qo_heads + head) * 2]);
+  float L = 0.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int d = 4 * threadIdx.x;
+  for (int s = 0; s < ns; ++s) {
+    const int64_t base = (int64_t)(first + s) * P.num_qo_heads + head;
+    const float wgt = __builtin_amdgcn_exp2f(P.part_ml[base * 2] - M);
+    L += wgt * P.part_ml[base * 2 + 1];
+    const f32x4 v = *reinterpret_cast<const f32x4*>(P.part_o + base * D + d);
+    acc += wgt * v;
+  }
+  const float inv = 1.0f / L;
+  const int64_t orow = ((int64_t)P.qo_indptr[b] * P.num_qo_heads + head) * D + d;
+  if constexpr (OUT_BF16) {
+    bf16x4 v = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv), (__bf16)(acc[2] * inv),
+                (__bf16)(acc[3] * inv)};
+    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(P.o) + orow) = v;
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(P.o) + orow) = acc * inv;
+  }
+}
+
+}  // namespace
+}  // namespace psw_dev

@@ -1,0 +1,32 @@
+// Instantiations of the paged attention kernels for head_dim 512.  Each
+// head_dim is its own translation unit so that it can be compiled with the
+// code-generation options that suit its register budget.
+#include "psw_attention.hpp"
+
+namespace psw_dev {
+namespace {
+
+template <bool SPLIT, bool OB>
+hipError_t launch_one(const AttnParams& p, int n_items, hipStream_t s) {
+  hipLaunchKernelGGL((attention_kernel<512, SPLIT, OB>), dim3(n_items * p.num_kv_heads), dim3(256),
+                     0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention_d512(bool split, bool out_bf16, const AttnParams& p, int n_items,
+                                hipStream_t s) {
+  if (n_items <= 0) return hipSuccess;
+  if (split) return out_bf16 ? launch_one<true, true>(p, n_items, s) : launch_one<true, false>(p, n_items, s);
+  return out_bf16 ? launch_one<false, true>(p, n_items, s) : launch_one<false, false>(p, n_items, s);
+}
+
+hipError_t launch_merge_d512(bool out_bf16, const MergeParams& p, int batch, hipStream_t s) {
+  const dim3 grid(batch * p.num_qo_heads);
+  if (out_bf16) hipLaunchKernelGGL((merge_kernel<512, true>), grid, dim3(512 / 4), 0, s, p);
+  else hipLaunchKernelGGL((merge_kernel<512, false>), grid, dim3(512 / 4), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace psw_dev

@@ -84,10 +84,12 @@ constexpr int kPrepItemInts = 6;
 constexpr int kPrepMaxTokens = 16;
 
 // Launchers (return the hipError_t of the launch).
-hipError_t launch_attention(int head_dim, bool split, bool out_bf16, const AttnParams& p,
-                            int n_items, hipStream_t s);
-hipError_t launch_merge(int head_dim, bool out_bf16, const MergeParams& p, int batch,
-                        hipStream_t s);
+hipError_t launch_attention_d256(bool split, bool out_bf16, const AttnParams& p, int n_items,
+                                 hipStream_t s);
+hipError_t launch_attention_d512(bool split, bool out_bf16, const AttnParams& p, int n_items,
+                                 hipStream_t s);
+hipError_t launch_merge_d256(bool out_bf16, const MergeParams& p, int batch, hipStream_t s);
+hipError_t launch_merge_d512(bool out_bf16, const MergeParams& p, int batch, hipStream_t s);
 hipError_t launch_prep_hd256(const PrepParams& p, int n_items, hipStream_t s);
 hipError_t launch_prep_hd512(const PrepParams& p, int n_items, hipStream_t s);
 hipError_t launch_rope_tables(float* c, float* s, int64_t positions, int64_t half, double theta,

@@ -224,7 +224,9 @@ int run_attention(psw_plan* plan, const psw_pool* pool, int64_t layer, const voi
   p.group_shift = group_shift_of(st.group);
   p.window_left = static_cast<int32_t>(wle);
   p.scale_log2 = sm_scale * 1.4426950408889634f;
-  hipError_t e = psw_dev::launch_attention(head_dim, decode, o_dtype == 1, p, n_items, s);
+  hipError_t e = head_dim == 256
+                     ? psw_dev::launch_attention_d256(decode, o_dtype == 1, p, n_items, s)
+                     : psw_dev::launch_attention_d512(decode, o_dtype == 1, p, n_items, s);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   if (decode) {
     psw_dev::MergeParams mp{};
@@ -234,7 +236,8 @@ int run_attention(psw_plan* plan, const psw_pool* pool, int64_t layer, const voi
     mp.qo_indptr = p.qo_indptr;
     mp.o = o;
     mp.num_qo_heads = st.num_qo_heads;
-    e = psw_dev::launch_merge(head_dim, o_dtype == 1, mp, st.batch, s);
+    e = head_dim == 256 ? psw_dev::launch_merge_d256(o_dtype == 1, mp, st.batch, s)
+                        : psw_dev::launch_merge_d512(o_dtype == 1, mp, st.batch, s);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
   return PSW_OK;
