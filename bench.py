@@ -168,7 +168,7 @@ def build_rows(torch, psw, synth, dev, want):
         pd = psw.pool_desc(pool, num_layers=1, num_pages=2048, page_size=16, num_kv_heads=1,
                            head_dim=512)
         plan = plan_of(case.qo_indptr, case.table, 16, 1, 512, 2048)
-        raw_k = synth.normal_bf16((16384, 1, 512), 0.25, synth.generator(33), device=dev)
+        raw_k = synth.normal_bf16((16384, 1, 512), 0.25, synth.generator(33, dev), device=dev)
         w = torch.ones(512, dtype=torch.bfloat16, device=dev)
         c, s = tables(512)
         psw.k_v_norm_rope_paged_prefill_hd512(plan, pd, 0, raw_k, w, c, s, 1e-6)

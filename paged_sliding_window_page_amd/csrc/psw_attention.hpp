@@ -30,6 +30,8 @@
 // that intersect a row's window are visited; whole tiles inside every row's
 // window skip the element mask.
 #pragma once
+#include <type_traits>
+
 #include "psw_device.hpp"
 
 namespace psw_dev {
@@ -64,10 +66,17 @@ __device__ __forceinline__ T ldu(const T* p) {
           (const __attribute__((address_space(4))) char*)p));
 }
 
+// Pin the computation of v before this point (an empty volatile use), so
+// later passes cannot sink it out of the block it is interleaved into.
+__device__ __forceinline__ void pin(float v) { asm volatile("" ::"v"(v)); }
+
 // Keep the compiler from if-converting a rare branch into straight-line code.
 __device__ __forceinline__ void rare_path() { asm volatile("" ::: "memory"); }
 
-template <int D, bool SPLIT, bool OUT_BF16>
+// PAGE16: the serving page size (16 slots), for which the page of every load
+// instruction is a compile-time function of the tile; otherwise page_size is a
+// runtime power of two >= 8.
+template <int D, bool SPLIT, bool OUT_BF16, bool PAGE16>
 __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
   constexpr int KT = D == 256 ? 64 : 32;  // keys per tile
   constexpr int NCH = D / 8;              // 16-B chunks per K row
@@ -81,8 +90,12 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
 
   // K and V^T tiles have separate double buffers: K[t+1] must be resident
   // while V[t-1] is still being read (see the pipeline below).
-  __shared__ __attribute__((aligned(1024))) char ks_lds[2][TILE];
-  __shared__ __attribute__((aligned(1024))) char vs_lds[2][TILE];
+  // Four distinct arrays (not one indexed array) so that the compiler can
+  // tell the stage being read from the stage the in-flight DMA is writing.
+  __shared__ __attribute__((aligned(1024))) char k_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[TILE];
 
   const int lane = threadIdx.x & 63;
   // wave index, explicitly wave-uniform so that per-wave address math is scalar
@@ -135,8 +148,8 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
 
   const char* kbase_g = reinterpret_cast<const char*>(P.pool + P.layer_off + (int64_t)kvh * P.ps.head);
   const char* vbase_g = kbase_g + P.ps.kv * 2;
-  const int pshift = P.ps.page_shift;
-  const int psize = P.ps.page_size;
+  const int pshift = PAGE16 ? 4 : P.ps.page_shift;
+  const int psize = PAGE16 ? 16 : P.ps.page_size;
   const int64_t page_bytes = P.ps.page * 2;
 
   const int jt0 = k_lo / KT;
@@ -171,27 +184,44 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
     const int idx = min((j0 >> pshift) + p, last_page);
     return base + (int64_t)ldu(pages + idx) * page_bytes;
   };
-  auto issue_k = [&](int st, int j0) {
-    char* kl = ks_lds[st];
-    const int slot0 = KT < psize ? (j0 & (psize - 1)) * D * 2 : 0;
+  auto issue_k = [&](char* kl, int j0) {
+    if constexpr (PAGE16) {
+      constexpr int NPT = KT / 16;
+      const char* pp[NPT];
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r)
-      lds_load16(page_ptr(kbase_g, j0, kpg[r]) + slot0 + koff[r], kl + (r * 4 + w) * 1024);
+      for (int p = 0; p < NPT; ++p) pp[p] = page_ptr(kbase_g, j0, p);
+#pragma unroll
+      for (int r = 0; r < ROUNDS; ++r)
+        lds_load16(pp[(r * 4 * KEYS_PER_LOAD) >> 4] + koff[r], kl + (r * 4 + w) * 1024);
+    } else {
+      const int slot0 = KT < psize ? (j0 & (psize - 1)) * D * 2 : 0;
+#pragma unroll
+      for (int r = 0; r < ROUNDS; ++r)
+        lds_load16(page_ptr(kbase_g, j0, kpg[r]) + slot0 + koff[r], kl + (r * 4 + w) * 1024);
+    }
   };
-  auto issue_v = [&](int st, int j0) {
-    char* vl = vs_lds[st];
-    const int slot0 = KT < psize ? (j0 & (psize - 1)) * 2 : 0;
+  auto issue_v = [&](char* vl, int j0) {
+    if constexpr (PAGE16) {
+      constexpr int NPT = KT / 16;
+      const char* pp[NPT];
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r)
-      lds_load16(page_ptr(vbase_g, j0, vpg[r]) + slot0 + voff[r], vl + (r * 4 + w) * 1024);
+      for (int p = 0; p < NPT; ++p) pp[p] = page_ptr(vbase_g, j0, p);
+#pragma unroll
+      for (int r = 0; r < ROUNDS; ++r)
+        lds_load16(pp[(8 * ((r * 4 * 64) / D)) >> 4] + voff[r], vl + (r * 4 + w) * 1024);
+    } else {
+      const int slot0 = KT < psize ? (j0 & (psize - 1)) * 2 : 0;
+#pragma unroll
+      for (int r = 0; r < ROUNDS; ++r)
+        lds_load16(page_ptr(vbase_g, j0, vpg[r]) + slot0 + voff[r], vl + (r * 4 + w) * 1024);
+    }
   };
   // Zero, in the V^T chunks this lane loaded itself, the keys at or past
   // kv_len (their pool slots may hold anything, NaN included, and 0 * NaN would
   // leak into O).  Called after this wave's loads have landed.
-  auto sanitize = [&](int st, int j0) {
+  auto sanitize = [&](char* vl, int j0) {
     if (j0 + KT <= kvl) return;
     rare_path();
-    char* vl = vs_lds[st];
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
       const int jc = j0 + 8 * (((r * 4 + w) * 64) / D);
@@ -233,8 +263,7 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
 
   // S^T for one tile.  K operands are read two k-steps ahead; the scheduling
   // barrier keeps the compiler from hoisting every read.
-  auto qk = [&](int st, f32x16* s) {
-    const char* kl = ks_lds[st];
+  auto qk = [&](const char* kl, f32x16* s) {
     bf16x8 a[3][KBLK];
     auto ld = [&](int ks, bf16x8* dst) {
 #pragma unroll
@@ -256,8 +285,7 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
     }
   };
   // O^T += V^T P^T for one tile (V^T operands read two steps ahead).
-  auto pv = [&](int st, const bf16x8* pb) {
-    const char* vl = vs_lds[st];
+  auto pv = [&](const char* vl, const bf16x8* pb) {
     constexpr int NSTEP = NT * DB;
     bf16x8 a[3];
     auto ld = [&](int i) { return *reinterpret_cast<const bf16x8*>(vl + vaddr(i / DB, i % DB)); };
@@ -303,19 +331,23 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
   };
 
   // ---- prologue: K[0], V[0] (and K[1]) resident ----
-  issue_k(0, jt0 * KT);
-  issue_v(0, jt0 * KT);
-  if (ntiles > 1) issue_k(1, (jt0 + 1) * KT);
+  issue_k(k_lds0, jt0 * KT);
+  issue_v(v_lds0, jt0 * KT);
+  if (ntiles > 1) issue_k(k_lds1, (jt0 + 1) * KT);
   __builtin_amdgcn_s_waitcnt(0);
-  sanitize(0, jt0 * KT);
+  sanitize(v_lds0, jt0 * KT);
   __syncthreads();
 
   // Pipeline, iteration t (K[t] and V[t-1] resident, V[t] / K[t+1] landed or
   // in flight):  S = Q K[t]^T;  softmax of tile t;  O += P[t-1] V[t-1];
   // rescale O if the running max rose;  then make V[t], K[t+1] resident and
   // start V[t+1], K[t+2].
-  for (int it = 0; it < ntiles; ++it) {
-    const int st = it & 1;
+  // One pipeline step for tile `it`; ST is its (compile-time) buffer parity.
+  auto step = [&](auto ST, int it) {
+    constexpr int st = decltype(ST)::value;
+    char* kcur = st ? k_lds1 : k_lds0;     // K[t]
+    char* vcur = st ? v_lds1 : v_lds0;     // V[t] (landing), later V[t+2]
+    char* vprev = st ? v_lds0 : v_lds1;    // V[t-1], then V[t+1]
     const int j0 = (jt0 + it) * KT;
     bf16x8 pcur[NT];
     float lsum = 0.0f;
@@ -323,39 +355,44 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
     bool need;
     {
       f32x16 s[KBLK];
-      qk(st, s);
-      // A tile inside every row's range of this wave needs no element mask;
-      // a tile outside every row's range is fully masked.
+      qk(kcur, s);
+      // A tile inside every row's range of this wave needs no element mask
+      // (masked tiles come back from tile_max already scaled).
       const bool full = wave_live && j0 >= k_lo && j0 + KT - 1 <= k_hi && j0 + KT - 1 <= w_pmin &&
                         (wl < 0 || w_pmax - j0 <= wl);
       const float tmax = tile_max(s, !full, j0);
       m_new = fmaxf(m_run, tmax);
       need = __any(m_new > m_run + kRescaleSlack);
       const float m_use = need ? m_new : m_run;
-      if (full) {
+      const float cmul = full ? c2 : 1.0f;
+      // PV of tile t-1, with the exponentials of tile t spread over its MFMAs
+      // (independent work for the VALU while the matrix unit is busy).
+      const char* vl = vprev;
+      constexpr int NSTEP = NT * DB;
+      constexpr int NE = KBLK * 16;  // exponentials per lane
+      bf16x8 a[3];
+      auto ld = [&](int i) { return *reinterpret_cast<const bf16x8*>(vl + vaddr(i / DB, i % DB)); };
+      a[0] = ld(0);
+      a[1] = ld(1);
 #pragma unroll
-        for (int kb = 0; kb < KBLK; ++kb)
+      for (int i = 0; i < NSTEP; ++i) {
+        if (i + 2 < NSTEP) a[(i + 2) % 3] = ld(i + 2);
+        oacc[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % 3], pprev[i / DB],
+                                                                oacc[i % DB], 0, 0, 0);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c2, -m_use));
-            s[kb][r] = p;
-            lsum += p;
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < KBLK; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(s[kb][r] - m_use);
-            s[kb][r] = p;
-            lsum += p;
-          }
+        for (int e = i * NE / NSTEP; e < (i + 1) * NE / NSTEP; ++e) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], cmul, -m_use));
+          s[e >> 4][e & 15] = p;
+          lsum += p;
+          pin(p);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i = 0; i < 8; ++i) pcur[t][i] = (__bf16)s[t >> 1][8 * (t & 1) + i];
-      pv(st ^ 1, pprev);
+      pin(lsum);
     }
     if (need) {
       rare_path();
@@ -372,14 +409,20 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
     // make V[t] and K[t+1] resident; the buffers of K[t] and V[t-1] are free
     // once every wave is past this barrier
     __builtin_amdgcn_s_waitcnt(0);
-    if (it >= 1) sanitize(st, j0);
+    if (it >= 1) sanitize(vcur, j0);
     __syncthreads();
     if (it + 1 < ntiles) {
-      issue_v(st ^ 1, j0 + KT);
-      if (it + 2 < ntiles) issue_k(st, j0 + 2 * KT);
+      issue_v(vprev, j0 + KT);
+      if (it + 2 < ntiles) issue_k(kcur, j0 + 2 * KT);
     }
+  };
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    step(std::integral_constant<int, 1>{}, it + 1);
   }
-  pv((ntiles - 1) & 1, pprev);
+  if (it < ntiles) step(std::integral_constant<int, 0>{}, it);
+  pv(((ntiles - 1) & 1) ? v_lds1 : v_lds0, pprev);
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!row_valid) return;

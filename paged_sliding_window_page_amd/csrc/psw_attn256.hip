@@ -8,8 +8,11 @@ namespace {
 
 template <bool SPLIT, bool OB>
 hipError_t launch_one(const AttnParams& p, int n_items, hipStream_t s) {
-  hipLaunchKernelGGL((attention_kernel<256, SPLIT, OB>), dim3(n_items * p.num_kv_heads), dim3(256),
-                     0, s, p);
+  const dim3 grid(n_items * p.num_kv_heads);
+  if (p.ps.page_size == 16)
+    hipLaunchKernelGGL((attention_kernel<256, SPLIT, OB, true>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((attention_kernel<256, SPLIT, OB, false>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
