@@ -184,19 +184,15 @@ def build_rows(torch, psw, synth, dev, want):
 
     # ---- decode through the prefill entry, 64 requests, both families ----
     if "decode_local_hd256" in want or "decode_global_hd512" in want:
-        kv = synth.uniform_lengths(64, 512, 8192, synth.generator(5))
         for d, name in ((256, "decode_local_hd256"), (512, "decode_global_hd512")):
             if name not in want:
                 continue
-            fam = synth.LOCAL if d == 256 else synth.GLOBAL
-            hkv = fam["num_kv_heads"]
-            gen = synth.generator(50 + d)
-            table = synth.random_page_table(kv, 16, 32768, gen)
-            numel = 32768 * 2 * hkv * 16 * d
-            pool = synth.normal_bf16((numel,), 0.25, synth.generator(500 + d, dev), device=dev)
-            q = synth.normal_bf16((64, 16, d), 0.25, gen).to(dev)
+            case = synth.decode_batch(d, dev)
+            kv, hkv = case.kv_lens, case.num_kv_heads
+            pool = case.pool
+            q = case.q.to(dev)
             o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
-            plan = plan_of(synth.lengths_to_indptr([1] * 64), table, 16, hkv, d, 32768)
+            plan = plan_of(case.qo_indptr, case.table, 16, hkv, d, 32768)
             pd = psw.pool_desc(pool, num_layers=1, num_pages=32768, page_size=16,
                                num_kv_heads=hkv, head_dim=d)
             wl = 1023 if d == 256 else -1

@@ -88,6 +88,10 @@ hipError_t launch_attention_d256(bool split, bool out_bf16, const AttnParams& p,
                                  hipStream_t s);
 hipError_t launch_attention_d512(bool split, bool out_bf16, const AttnParams& p, int n_items,
                                  hipStream_t s);
+// One-token decode split kernel: one wave per (split, KV head); writes the same
+// partials as the split attention kernels.  Needs H_q / H_kv <= kDecodeMaxGroup.
+constexpr int kDecodeMaxGroup = 16;
+hipError_t launch_decode(int head_dim, const AttnParams& p, int n_units, hipStream_t s);
 hipError_t launch_merge_d256(bool out_bf16, const MergeParams& p, int batch, hipStream_t s);
 hipError_t launch_merge_d512(bool out_bf16, const MergeParams& p, int batch, hipStream_t s);
 hipError_t launch_prep_hd256(const PrepParams& p, int n_items, hipStream_t s);

@@ -172,7 +172,7 @@ int run_attention(psw_plan* plan, const psw_pool* pool, int64_t layer, const voi
   const int kv_tile = psw::kv_tile_for(head_dim);
   if (decode) {
     if (plan->decode.window_left != wle)
-      psw::build_decode_schedule(st, wle, kv_tile, &plan->decode);
+      psw::build_decode_schedule(st, wle, &plan->decode);
   } else {
     if (plan->prefill.window_left != wle)
       psw::build_prefill_schedule(st, wle, kv_tile, &plan->prefill);
@@ -224,9 +224,12 @@ int run_attention(psw_plan* plan, const psw_pool* pool, int64_t layer, const voi
   p.group_shift = group_shift_of(st.group);
   p.window_left = static_cast<int32_t>(wle);
   p.scale_log2 = sm_scale * 1.4426950408889634f;
-  hipError_t e = head_dim == 256
-                     ? psw_dev::launch_attention_d256(decode, o_dtype == 1, p, n_items, s)
-                     : psw_dev::launch_attention_d512(decode, o_dtype == 1, p, n_items, s);
+  hipError_t e;
+  if (decode && st.group <= psw_dev::kDecodeMaxGroup)
+    e = psw_dev::launch_decode(head_dim, p, n_items * st.num_kv_heads, s);
+  else
+    e = head_dim == 256 ? psw_dev::launch_attention_d256(decode, o_dtype == 1, p, n_items, s)
+                        : psw_dev::launch_attention_d512(decode, o_dtype == 1, p, n_items, s);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   if (decode) {
     psw_dev::MergeParams mp{};

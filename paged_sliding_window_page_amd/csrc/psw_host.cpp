@@ -234,7 +234,7 @@ void build_prefill_schedule(const PlanState& st, int64_t wl, int32_t kv_tile, Pr
   out->total_tiles = total;
 }
 
-void build_decode_schedule(const PlanState& st, int64_t wl, int32_t kv_tile, DecodeSchedule* out) {
+void build_decode_schedule(const PlanState& st, int64_t wl, DecodeSchedule* out) {
   // keys each request must read: the window (or everything) ending at p = kv_len - 1
   std::vector<int64_t> lo(st.batch), n(st.batch);
   int64_t key_heads = 0;
@@ -244,10 +244,14 @@ void build_decode_schedule(const PlanState& st, int64_t wl, int32_t kv_tile, Dec
     n[b] = p - lo[b] + 1;
     key_heads += n[b] * st.num_kv_heads;
   }
-  // About 1024 work-groups, each a whole number of KV tiles so that no tile is
-  // shared between two splits.
-  const int64_t unit = std::max<int64_t>(kv_tile, 2 * kDecodeKeysPerSubtile);
-  int64_t chunk = (key_heads + 1023) / 1024;
+  // One work-group per (split, KV head), about kDecodeTargetUnits of them
+  // (2 to 4 waves each: two rounds of the 256 CUs at 8 waves per CU).  A split
+  // writes group x head_dim fp32 partials that the merge reads back, against
+  // 4 x head_dim bytes of K and V per key: at least 16 x group keys per split
+  // keeps that traffic under 1/16 of the K/V stream.
+  const int64_t unit = kDecodeSplitUnit;
+  int64_t chunk = (key_heads + kDecodeTargetUnits - 1) / kDecodeTargetUnits;
+  chunk = std::max<int64_t>(chunk, 16 * int64_t(st.group));
   chunk = std::max<int64_t>(unit, (chunk + unit - 1) / unit * unit);
   out->items.clear();
   out->req_splits.assign(2 * st.batch, 0);

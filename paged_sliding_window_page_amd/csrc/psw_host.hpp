@@ -40,7 +40,9 @@ int check_pool(const psw_pool* pool, bool need_base);
 constexpr int kPrefillRows = 128;          // query rows (token x head) per work-group
 constexpr int kKvTile256 = 64;             // keys per prefill tile at head_dim 256
 constexpr int kKvTile512 = 32;             // keys per prefill tile at head_dim 512
-constexpr int kDecodeKeysPerSubtile = 32;  // keys one decode wave handles per step
+constexpr int kDecodeTile = 16;            // keys per decode MFMA step (one wave per split)
+constexpr int kDecodeSplitUnit = 64;       // split boundaries are multiples of this key index
+constexpr int kDecodeTargetUnits = 2048;   // decode (split, KV head) work-groups aimed for
 constexpr int kMaxGroup = 32;
 
 int derive_tile_q(int64_t group, int64_t head_dim, int32_t* tile_q);
@@ -84,8 +86,7 @@ struct DecodeSchedule {
   std::vector<int32_t> req_splits;   // pairs (first partial slot, number of splits) per request
   int32_t num_partials = 0;
 };
-void build_decode_schedule(const PlanState& st, int64_t window_left, int32_t kv_tile,
-                           DecodeSchedule* out);
+void build_decode_schedule(const PlanState& st, int64_t window_left, DecodeSchedule* out);
 
 // Prep work items: up to 16 consecutive positions of one request inside one
 // page, as (request, first global token, tokens, page id, first slot, first

@@ -32,6 +32,7 @@ __all__ = [
     "attention_case",
     "PrepCase",
     "prep_case",
+    "decode_batch",
     "LOCAL",
     "GLOBAL",
 ]
@@ -144,6 +145,26 @@ def attention_case(seed: int, qo_lens, kv_lens, *, num_qo_heads: int, num_kv_hea
     return AttentionCase(num_qo_heads, num_kv_heads, head_dim, page_size, num_pages,
                          num_layers, layer, list(map(int, qo_lens)), list(map(int, kv_lens)),
                          lengths_to_indptr(qo_lens), table, q, pool)
+
+
+def decode_batch(head_dim: int, device, num_requests: int = 64, lo: int = 512,
+                 hi: int = 8192, num_pages: int = 32768, seed: int = 5) -> AttentionCase:
+    """One-token decode batch of a serving step: ``num_requests`` requests with
+    KV lengths ~ U[lo, hi] (one query each), random page tables over a pool of
+    ``num_pages`` 16-slot pages, Q and the whole pool ~ N(0, 0.25^2).  The
+    pool is drawn directly on ``device`` (it is several GiB at head_dim 256);
+    Q stays on the CPU like the other cases."""
+    fam = LOCAL if head_dim == 256 else GLOBAL
+    hkv = fam["num_kv_heads"]
+    kv = uniform_lengths(num_requests, lo, hi, generator(seed))
+    gen = generator(50 + head_dim)
+    table = random_page_table(kv, 16, num_pages, gen)
+    numel = pool_numel(1, num_pages, hkv, 16, head_dim)
+    pool = normal_bf16((numel,), 0.25, generator(500 + head_dim, device), device=device)
+    q = normal_bf16((num_requests, fam["num_qo_heads"], head_dim), 0.25, gen)
+    return AttentionCase(fam["num_qo_heads"], hkv, head_dim, 16, num_pages, 1, 0,
+                         [1] * num_requests, list(map(int, kv)),
+                         lengths_to_indptr([1] * num_requests), table, q, pool)
 
 
 @dataclass

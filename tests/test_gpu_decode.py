@@ -1,0 +1,113 @@
+"""GPU parity of one-token decode through the prefill entries, against the fp64
+oracle, through the C ABI.
+
+Decode is the prefill entry called with one query per request (PR
+"feat(gemma4): paged KV serving across both attention families", Description).
+The library runs it as split-KV partials plus a merge; these cases cover the
+page-size modes of the decode kernel (pages of 8, 16 and >= 32 slots), the GQA
+group widths (up to 16 query heads per KV head in the decode kernel, 32 through
+the general split kernel), windows that start mid-tile, NaN outside the keys
+a request may read, and the full-size 64-request batch on sampled requests.
+Gate and tolerances: tests/gpu_util.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import (SENTINEL, bits_tensor, check_close, flat_k_index, flat_v_index, geom_of,
+                      oracle_attention, run_attention, say)
+
+pytestmark = pytest.mark.gpu
+
+LOCAL = synth.LOCAL
+GLOBAL = synth.GLOBAL
+
+
+def _case(hd, seed, kv, **kw):
+    a = dict(LOCAL if hd == 256 else GLOBAL)
+    a.update(kw)
+    return synth.attention_case(seed, [1] * len(kv), kv, **a)
+
+
+KV_MIX = [1, 2, 15, 16, 17, 31, 32, 33, 64, 65, 300, 1500]
+
+
+@pytest.mark.parametrize("hd", [256, 512])
+@pytest.mark.parametrize("page_size", [8, 16, 32, 64])
+def test_decode_page_sizes(hd, page_size):
+    case = _case(hd, 61, KV_MIX, page_size=page_size)
+    wl = 100 if hd == 256 else -1
+    gpu = run_attention(case, window_left=wl, label=f"decode P={page_size}")
+    check_close(gpu, oracle_attention(case, window_left=wl), f"decode hd{hd} P={page_size}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (16, 8), (16, 4), (8, 1), (16, 1), (32, 1)])
+def test_decode_group_sizes(hq, hkv):
+    case = _case(256, 63, [40, 700, 129], num_qo_heads=hq, num_kv_heads=hkv)
+    gpu = run_attention(case, window_left=200, label=f"decode group {hq // hkv}")
+    check_close(gpu, oracle_attention(case, window_left=200), f"decode group {hq // hkv}")
+
+
+@pytest.mark.parametrize("wl", [-1, 0, 1, 30, 31, 32, 33, 63, 64, 1023, 10 ** 6])
+def test_decode_window_edges(wl):
+    case = _case(256, 67, KV_MIX)
+    gpu = run_attention(case, window_left=wl, label=f"decode wl={wl}")
+    check_close(gpu, oracle_attention(case, window_left=wl), f"decode wl={wl}")
+
+
+def _poison_outside(case, wl):
+    """Pool bits with NaN in every page outside the tables, every slot past a
+    request's KV length and every key before its window."""
+    g = geom_of(case)
+    bits = oracle.bf16_bits(case.pool).copy()
+    used = set(case.table.kv_page_indices.tolist())
+    by_page = bits.reshape(g.num_layers, g.num_pages, -1)
+    for p in range(g.num_pages):
+        if p not in used:
+            by_page[:, p] = SENTINEL
+    t = case.table
+    d = np.arange(g.head_dim)
+    P = g.page_size
+    for b, kv in enumerate(case.kv_lens):
+        pages = t.kv_page_indices[t.kv_page_indptr[b]:t.kv_page_indptr[b + 1]]
+        first = 0 if wl < 0 else max(0, kv - 1 - wl)
+        dead = list(range(first)) + list(range(kv, len(pages) * P))
+        for key in dead:
+            page, slot = int(pages[key // P]), key % P
+            for hh in range(g.num_kv_heads):
+                bits[flat_k_index(g, case.layer, page, hh, slot, d)] = SENTINEL
+                bits[flat_v_index(g, case.layer, page, hh, d, slot)] = SENTINEL
+    return bits
+
+
+@pytest.mark.parametrize("hd,page_size", [(256, 16), (256, 8), (256, 64), (512, 16)])
+def test_decode_nan_outside_the_keys_never_leaks(hd, page_size):
+    case = _case(hd, 71, [1, 37, 70, 100, 250], page_size=page_size, num_pages=120)
+    wl = 45 if hd == 256 else -1
+    bits = _poison_outside(case, wl)
+    clean = run_attention(case, window_left=wl, label="decode clean")
+    dirty = run_attention(case, window_left=wl, pool=bits_tensor(bits), label="decode poisoned")
+    np.testing.assert_array_equal(dirty, clean)
+    check_close(clean, oracle_attention(case, window_left=wl), "decode poison case")
+
+
+@pytest.mark.parametrize("hd", [256, 512])
+def test_decode_full_size_sampled(hd):
+    """The 64-request decode batch (KV ~ U[512, 8192], pool of 32768 pages)
+    in the launch configuration the benchmark times; 12 requests (all 16 heads)
+    are checked against the oracle."""
+    dev = torch.device("cuda", 0)
+    case = synth.decode_batch(hd, dev)
+    wl = 1023 if hd == 256 else -1
+    gpu = run_attention(case, window_left=wl, pool=case.pool, label=f"decode full hd{hd}")
+    say("[gpu] copying the pool to the host for the oracle")
+    host = synth.AttentionCase(**{**case.__dict__, "pool": case.pool.cpu()})
+    rng = np.random.default_rng(hd)
+    reqs = sorted(set(rng.integers(0, 64, 10).tolist()) | {int(np.argmax(case.kv_lens)),
+                                                            int(np.argmin(case.kv_lens))})
+    samples = [(b, h) for b in reqs for h in range(16)]
+    ref = oracle_attention(host, window_left=wl, samples=samples)
+    idx = tuple(np.array(samples).T)
+    check_close(gpu[idx], ref[idx], f"decode full hd{hd}")
