@@ -106,7 +106,8 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
   const int item = blockIdx.x / hkv;
   const int kvh = blockIdx.x - item * hkv;
   const int b = ldu(P.items + 4 * item + 0);
-  const int t0 = ldu(P.items + 4 * item + 1);
+  // split mode (one query per request): field 1 is the partial slot, t0 = 0
+  const int t0 = SPLIT ? 0 : ldu(P.items + 4 * item + 1);
   const int k_lo = ldu(P.items + 4 * item + 2);
   const int k_hi = ldu(P.items + 4 * item + 3);
   const int q_beg = ldu(P.qo_indptr + b);
@@ -428,7 +429,8 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
   if (!row_valid) return;
   // lane (n, h), O^T block db, register r holds d = 32*db + 8*(r/4) + 4*h + r%4
   if constexpr (SPLIT) {
-    const int64_t base = ((int64_t)item * P.num_qo_heads + head);
+    const int slot = ldu(P.items + 4 * item + 1);
+    const int64_t base = ((int64_t)slot * P.num_qo_heads + head);
     float* po = P.part_o + base * D + 4 * h;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -471,18 +473,46 @@ __global__ __launch_bounds__(D / 4) void merge_kernel(MergeParams P) {
   const int head = blockIdx.x - b * P.num_qo_heads;
   const int first = P.req_splits[2 * b];
   const int ns = P.req_splits[2 * b + 1];
+  // Splits are combined 8 at a time with all their loads issued first, so the
+  // loop runs at memory throughput rather than one load latency per split.
+  constexpr int U = 8;
+  const float* ml = P.part_ml + ((int64_t)first * P.num_qo_heads + head) * 2;
+  const int64_t ml_stride = 2 * (int64_t)P.num_qo_heads;
   float M = kNegBig;
-  for (int s = 0; s < ns; ++s)
-    M = fmaxf(M, P.part_ml[((int64_t)(first + s) * P.num_qo_heads + head) * 2]);
+  int s = 0;
+  for (; s + U <= ns; s += U) {
+    float m[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) m[u] = ml[(s + u) * ml_stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = fmaxf(M, m[u]);
+  }
+  for (; s < ns; ++s) M = fmaxf(M, ml[s * ml_stride]);
   float L = 0.0f;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   const int d = 4 * threadIdx.x;
-  for (int s = 0; s < ns; ++s) {
-    const int64_t base = (int64_t)(first + s) * P.num_qo_heads + head;
-    const float wgt = __builtin_amdgcn_exp2f(P.part_ml[base * 2] - M);
-    L += wgt * P.part_ml[base * 2 + 1];
-    const f32x4 v = *reinterpret_cast<const f32x4*>(P.part_o + base * D + d);
-    acc += wgt * v;
+  const float* po = P.part_o + ((int64_t)first * P.num_qo_heads + head) * D + d;
+  const int64_t po_stride = (int64_t)P.num_qo_heads * D;
+  for (s = 0; s + U <= ns; s += U) {
+    float m[U], l[U];
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      m[u] = ml[(s + u) * ml_stride];
+      l[u] = ml[(s + u) * ml_stride + 1];
+      v[u] = *reinterpret_cast<const f32x4*>(po + (s + u) * po_stride);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wgt = __builtin_amdgcn_exp2f(m[u] - M);
+      L += wgt * l[u];
+      acc += wgt * v[u];
+    }
+  }
+  for (; s < ns; ++s) {
+    const float wgt = __builtin_amdgcn_exp2f(ml[s * ml_stride] - M);
+    L += wgt * ml[s * ml_stride + 1];
+    acc += wgt * *reinterpret_cast<const f32x4*>(po + s * po_stride);
   }
   const float inv = 1.0f / L;
   const int64_t orow = ((int64_t)P.qo_indptr[b] * P.num_qo_heads + head) * D + d;

@@ -31,6 +31,8 @@ namespace {
 constexpr float kNegBigD = -1.0e30f;
 constexpr float kSlackD = 8.0f;  // log2 units: rescale O only past a 256x rise
 constexpr int kTK = 32;          // keys per tile
+constexpr int kDW = 128;         // head dims per wave
+constexpr int kNST = 2;          // register stages of the K/V tile pipeline
 
 template <typename T>
 __device__ __forceinline__ T ldu(const T* p) {
@@ -38,14 +40,32 @@ __device__ __forceinline__ T ldu(const T* p) {
       (const __attribute__((address_space(4))) char*)p);
 }
 
+// Streaming 16-byte load: every K/V byte is read once, so the loads carry the
+// non-temporal hint (plain loads that allocate in the caches sustain markedly
+// less HBM read bandwidth on this part).
+__device__ __forceinline__ bf16x8 ld_stream(const char* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, in order
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void for_stages(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    for_stages<N, I + 1>(f);
+  }
+}
+
 // PMODE: 0 = pages smaller than 16 slots (per-lane page ids), 1 = 16-slot
 // pages (two wave-uniform page ids per tile), 2 = pages of 32 slots or more
 // (one wave-uniform page id per tile).
 template <int D, int PMODE>
-__global__ __launch_bounds__(64 * (D / 128)) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(AttnParams P) {
-  constexpr int W = D / 128;  // waves; wave w owns dims [128 w, 128 w + 128)
-  constexpr int KS = 4;       // 32-dim k-steps of the per-wave QK
-  constexpr int DB = 8;       // 16-dim blocks of the per-wave O^T
+__global__ __launch_bounds__(64 * (D / kDW)) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_kernel(AttnParams P) {
+  constexpr int W = D / kDW;   // waves; wave w owns dims [kDW w, kDW (w + 1))
+  constexpr int KS = kDW / 32; // 32-dim k-steps of the per-wave QK
+  constexpr int DB = kDW / 16; // 16-dim blocks of the per-wave O^T
   __shared__ f32x4 sx[2][W][2][64];  // partial S^T exchange [buffer][wave][block][lane]
 
   const int lane = threadIdx.x & 63;
@@ -53,18 +73,18 @@ __global__ __launch_bounds__(64 * (D / 128)) __attribute__((amdgpu_waves_per_eu(
   const int n = lane & 15;   // query row (head within the group); K row; V^T dim
   const int q4 = lane >> 4;  // lane quarter
   const int hkv = P.num_kv_heads;
-  const int unit = blockIdx.x;
-  const int slot = unit / hkv;
-  const int kvh = unit - slot * hkv;
-  const int b = ldu(P.items + 4 * slot + 0);
-  const int k_lo = ldu(P.items + 4 * slot + 2);
-  const int k_hi = ldu(P.items + 4 * slot + 3);
+  const int item = blockIdx.x / hkv;
+  const int kvh = blockIdx.x - item * hkv;
+  const int b = ldu(P.items + 4 * item + 0);
+  const int slot = ldu(P.items + 4 * item + 1);  // partial slot
+  const int k_lo = ldu(P.items + 4 * item + 2);
+  const int k_hi = ldu(P.items + 4 * item + 3);
   const int q_row = ldu(P.qo_indptr + b);  // qo_len == 1
   const int32_t* pages = P.kv_page_indices + ldu(P.kv_page_indptr + b);
   const int group = 1 << P.group_shift;
   const bool row_valid = n < group;
   const int head = kvh * group + (row_valid ? n : 0);
-  const int dim0 = 128 * w;
+  const int dim0 = kDW * w;
 
   // Q^T operand (B of S^T = K Q^T): lane (row n, quarter q4) holds
   // Q[n][dim0 + 32 ks + 8 q4 .. +8]
@@ -125,12 +145,12 @@ __global__ __launch_bounds__(64 * (D / 128)) __attribute__((amdgpu_waves_per_eu(
     tile_addr(j0, &kp0, &kp1, &vp);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kr[0][ks] = *reinterpret_cast<const bf16x8*>(kp0 + 64 * ks);
-      kr[1][ks] = *reinterpret_cast<const bf16x8*>(kp1 + 64 * ks);
+      kr[0][ks] = ld_stream(kp0 + 64 * ks);
+      kr[1][ks] = ld_stream(kp1 + 64 * ks);
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      vr[db] = *reinterpret_cast<const bf16x8*>(vp + (int64_t)db * 16 * psize * 2);
+      vr[db] = ld_stream(vp + (int64_t)db * 16 * psize * 2);
   };
 
   f32x4 oacc[DB];
@@ -141,14 +161,18 @@ __global__ __launch_bounds__(64 * (D / 128)) __attribute__((amdgpu_waves_per_eu(
 
   const int jt0 = k_lo / kTK;
   const int ntiles = k_hi / kTK - jt0 + 1;
-  bf16x8 kr[2][2][KS];
-  bf16x8 vr[2][DB];
-  load(jt0 * kTK, kr[0], vr[0]);
+  bf16x8 kr[kNST][2][KS];
+  bf16x8 vr[kNST][DB];
+  // prologue: the first kNST - 1 tiles in flight
+#pragma unroll
+  for (int t = 0; t < kNST - 1; ++t)
+    if (t < ntiles) load((jt0 + t) * kTK, kr[t], vr[t]);
 
   auto step = [&](auto STAGE, int it) {
-    constexpr int cb = decltype(STAGE)::value;
+    constexpr int cb = decltype(STAGE)::value;  // == it % kNST
+    constexpr int nb = (cb + kNST - 1) % kNST;  // stage of tile it + kNST - 1
     const int j0 = (jt0 + it) * kTK;
-    if (it + 1 < ntiles) load(j0 + kTK, kr[cb ^ 1], vr[cb ^ 1]);
+    if (it + kNST - 1 < ntiles) load(j0 + (kNST - 1) * kTK, kr[nb], vr[nb]);
     f32x4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -156,17 +180,20 @@ __global__ __launch_bounds__(64 * (D / 128)) __attribute__((amdgpu_waves_per_eu(
       s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[cb][1][ks], qf[ks], s[1], 0, 0, 0);
     }
     if constexpr (W > 1) {
-      sx[cb][w][0][lane] = s[0];
-      sx[cb][w][1][lane] = s[1];
+      // two exchange buffers alternate by tile parity: a wave rewrites one
+      // only after the next barrier, which every wave reaches after reading it
+      const int xb = it & 1;
+      sx[xb][w][0][lane] = s[0];
+      sx[xb][w][1][lane] = s[1];
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-      s[0] = sx[cb][0][0][lane];
-      s[1] = sx[cb][0][1][lane];
+      s[0] = sx[xb][0][0][lane];
+      s[1] = sx[xb][0][1][lane];
 #pragma unroll
       for (int v = 1; v < W; ++v) {
-        s[0] += sx[cb][v][0][lane];
-        s[1] += sx[cb][v][1][lane];
+        s[0] += sx[xb][v][0][lane];
+        s[1] += sx[xb][v][1][lane];
       }
     }
     // lane (row n, q4): s[sb][r] is the score of key j0 + 8 q4 + 4 sb + r
@@ -212,12 +239,13 @@ __global__ __launch_bounds__(64 * (D / 128)) __attribute__((amdgpu_waves_per_eu(
     for (int db = 0; db < DB; ++db)
       oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[cb][db], pb, oacc[db], 0, 0, 0);
   };
+  // main loop unrolled by the stage count so every stage index is a constant
   int it = 0;
-  for (; it + 1 < ntiles; it += 2) {
-    step(std::integral_constant<int, 0>{}, it);
-    step(std::integral_constant<int, 1>{}, it + 1);
-  }
-  if (it < ntiles) step(std::integral_constant<int, 0>{}, it);
+  for (; it + kNST <= ntiles; it += kNST)
+    for_stages<kNST>([&](auto st) { step(st, it + decltype(st)::value); });
+  for_stages<kNST>([&](auto st) {
+    if (it + decltype(st)::value < ntiles) step(st, it + decltype(st)::value);
+  });
 
   // row sums: each lane holds the part over its keys; add the four quarters
   float l_tot = l_run + __shfl_xor(l_run, 16);
@@ -236,7 +264,7 @@ __global__ __launch_bounds__(64 * (D / 128)) __attribute__((amdgpu_waves_per_eu(
 
 template <int D>
 hipError_t launch_d(const AttnParams& p, int n_units, hipStream_t s) {
-  const dim3 grid(n_units), block(64 * (D / 128));
+  const dim3 grid(n_units), block(64 * (D / kDW));
   if (p.ps.page_size >= 32)
     hipLaunchKernelGGL((decode_kernel<D, 2>), grid, block, 0, s, p);
   else if (p.ps.page_size == 16)

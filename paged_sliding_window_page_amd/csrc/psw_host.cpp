@@ -253,22 +253,37 @@ void build_decode_schedule(const PlanState& st, int64_t wl, DecodeSchedule* out)
   int64_t chunk = (key_heads + kDecodeTargetUnits - 1) / kDecodeTargetUnits;
   chunk = std::max<int64_t>(chunk, 16 * int64_t(st.group));
   chunk = std::max<int64_t>(unit, (chunk + unit - 1) / unit * unit);
-  out->items.clear();
+  // Each request's keys are cut into ceil(n / chunk) nearly equal splits at
+  // multiples of kDecodeSplitUnit (absolute key index, so no KV tile is read
+  // by two splits).  Items are then ordered longest first, so the short
+  // splits fill in behind the long ones at the end of the launch.
+  struct Split { int32_t b, slot, lo, hi; };
+  std::vector<Split> splits;
   out->req_splits.assign(2 * st.batch, 0);
   int32_t slot = 0;
   for (int32_t b = 0; b < st.batch; ++b) {
     const int32_t first = slot;
-    // split boundaries on multiples of the chunk in absolute key index
     const int64_t end = lo[b] + n[b];
-    for (int64_t k0 = lo[b]; k0 < end;) {
-      const int64_t k1 = std::min((k0 / chunk + 1) * chunk, end);
-      out->items.insert(out->items.end(), {b, 0, int32_t(k0), int32_t(k1 - 1)});
-      ++slot;
+    const int64_t ns = (n[b] + chunk - 1) / chunk;
+    int64_t k0 = lo[b];
+    for (int64_t i = 1; i <= ns; ++i) {
+      int64_t k1 = end;
+      if (i < ns) {
+        k1 = (lo[b] + i * n[b] / ns + unit / 2) / unit * unit;
+        if (k1 <= k0 || k1 >= end) continue;
+      }
+      splits.push_back({b, slot++, int32_t(k0), int32_t(k1 - 1)});
       k0 = k1;
     }
     out->req_splits[2 * b] = first;
     out->req_splits[2 * b + 1] = slot - first;
   }
+  std::stable_sort(splits.begin(), splits.end(), [](const Split& x, const Split& y) {
+    return x.hi - x.lo > y.hi - y.lo;
+  });
+  out->items.clear();
+  out->items.reserve(4 * splits.size());
+  for (const Split& sp : splits) out->items.insert(out->items.end(), {sp.b, sp.slot, sp.lo, sp.hi});
   out->num_partials = slot;
   out->window_left = wl;
   out->chunk = static_cast<int32_t>(chunk);

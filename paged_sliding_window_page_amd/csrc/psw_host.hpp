@@ -77,8 +77,9 @@ struct PrefillSchedule {
 void build_prefill_schedule(const PlanState& st, int64_t window_left, int32_t kv_tile,
                             PrefillSchedule* out);
 
-// Decode (qo_len == 1 everywhere) split-KV schedule.  Items are quads like the
-// prefill ones (request, 0, first key, last key); item i writes partial slot i.
+// Decode (qo_len == 1 everywhere) split-KV schedule.  Items are quads
+// (request, partial slot, first key, last key), longest first; the slots of a
+// request are consecutive, in key order.
 struct DecodeSchedule {
   int64_t window_left = -2;
   int32_t chunk = 0;                 // keys per split
