@@ -242,6 +242,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--rows", type=str, default="")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first copy a buffer of this many MiB (device to device) three "
+                         "times: the reference for scaling hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -256,10 +259,16 @@ def main():
                 "decode_local_hd256", "decode_global_hd512"]
     want = set(args.rows.split(",")) if args.rows else set(all_rows)
     dev = torch.device("cuda", 0)
+    flush = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
     log("building workloads ...")
     rows = build_rows(torch, psw, synth, dev, want)
     rows.sort(key=lambda r: all_rows.index(r.name))
-    flush = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        del src, dst
     torch.cuda.synchronize()
     log("warmup ...")
     for _ in range(args.warmup):

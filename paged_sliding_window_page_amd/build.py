@@ -47,7 +47,8 @@ def _flags():
 # rescale touch them without AGPR round trips; Q fragments then go to AGPRs,
 # which the MFMA reads directly.  (At head_dim 512, O alone fills 256
 # registers, so it stays in AGPRs.)
-EXTRA = {"psw_attn256.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"psw_attn256.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "psw_attn512.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -70,6 +70,17 @@ __device__ __forceinline__ T ldu(const T* p) {
 // later passes cannot sink it out of the block it is interleaved into.
 __device__ __forceinline__ void pin(float v) { asm volatile("" ::"v"(v)); }
 
+// Work-group barrier over LDS traffic only: waits for this wave's own LDS
+// reads and writes (lgkmcnt) but not for tile loads still in flight into LDS
+// (a workgroup fence would also wait for those, vmcnt).  The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Keep the compiler from if-converting a rare branch into straight-line code.
 __device__ __forceinline__ void rare_path() { asm volatile("" ::: "memory"); }
 
@@ -78,15 +89,24 @@ __device__ __forceinline__ void rare_path() { asm volatile("" ::: "memory"); }
 // runtime power of two >= 8.
 template <int D, bool SPLIT, bool OUT_BF16, bool PAGE16>
 __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
+  // Four waves of 32 query rows.  At head_dim 512 the dims are split between
+  // the two waves of a row group (each keeps O^T and Q for 256 dims, which
+  // leaves room in its registers) and the pair's partial scores are summed
+  // through LDS: 2 row groups x 2 dim halves, 64 rows per work-group.
+  constexpr int DH = D == 512 ? 2 : 1;    // dim halves
+  constexpr int DW = D / DH;              // dims per wave
+  constexpr int NW = 4;                   // waves per work-group
+  constexpr int RG = NW / DH;             // row groups
   constexpr int KT = D == 256 ? 64 : 32;  // keys per tile
   constexpr int NCH = D / 8;              // 16-B chunks per K row
   constexpr int KBLK = KT / 32;           // S^T 32-key blocks per tile
   constexpr int NT = KT / 16;             // PV steps (16 keys each) per tile
-  constexpr int DB = D / 32;              // O^T 32-row blocks
-  constexpr int KS = D / 16;              // QK k-steps
+  constexpr int DB = DW / 32;             // O^T 32-row blocks per wave
+  constexpr int KS = DW / 16;             // QK k-steps per wave
   constexpr int TILE = KT * D * 2;        // bytes of one K (or V^T) tile: 32 KiB
-  constexpr int ROUNDS = TILE / (256 * 16);
+  constexpr int ROUNDS = TILE / (NW * 64 * 16);
   constexpr int KEYS_PER_LOAD = 1024 / (D * 2);  // keys one K load instruction covers
+  static_assert((NW * KEYS_PER_LOAD) % 16 == 0 || 16 % (NW * KEYS_PER_LOAD) == 0, "");
 
   // K and V^T tiles have separate double buffers: K[t+1] must be resident
   // while V[t-1] is still being read (see the pipeline below).
@@ -96,10 +116,14 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
   __shared__ __attribute__((aligned(1024))) char k_lds1[TILE];
   __shared__ __attribute__((aligned(1024))) char v_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) char v_lds1[TILE];
+  // partial S^T of each wave, [wave][register quad][lane] (conflict-free)
+  __shared__ f32x4 xs[DH > 1 ? NW : 1][4 * KBLK][64];
 
   const int lane = threadIdx.x & 63;
   // wave index, explicitly wave-uniform so that per-wave address math is scalar
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rg = w & (RG - 1);  // row group
+  const int dh = w / RG;        // dim half (0 unless D == 512)
   const int n = lane & 31;
   const int h = lane >> 5;
   const int hkv = P.num_kv_heads;
@@ -122,7 +146,7 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
   const int wl = P.window_left;
 
   // this lane's query row: token t0 + tl, head kvh*group + hh
-  const int tl = w * tok_w + (n >> gs);
+  const int tl = rg * tok_w + (n >> gs);
   const int hh = n & ((1 << gs) - 1);
   const int tok = t0 + tl;
   const bool row_valid = tok < qo_len;
@@ -132,14 +156,15 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
   const int hi_n = row_valid ? min(k_hi, pos) : -1;
   const int lo_n = max(k_lo, wl >= 0 ? pos - wl : 0);
   // the same range, over every row of this wave (for whole-tile decisions)
-  const int wt0 = t0 + w * tok_w;
+  const int wt0 = t0 + rg * tok_w;
   const int w_pmin = start + wt0;
   const int w_pmax = start + min(wt0 + tok_w, qo_len) - 1;
   const bool wave_live = wt0 < qo_len;
 
   bf16x8 qf[KS];
   {
-    const __bf16* qrow = P.q + ((int64_t)(q_beg + (row_valid ? tok : 0)) * P.num_qo_heads + head) * D + 8 * h;
+    const __bf16* qrow = P.q + ((int64_t)(q_beg + (row_valid ? tok : 0)) * P.num_qo_heads + head) * D +
+                         DW * dh + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
@@ -168,7 +193,7 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
   int kpg[ROUNDS], vpg[ROUNDS];     // page of the tile (wave-uniform)
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
-    const int ins = r * 4 + w;
+    const int ins = r * NW + w;
     const int u = ins * 64 + lane;
     const int key = u / NCH;
     const int c = (u % NCH) ^ kswz(key);
@@ -193,12 +218,12 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
       for (int p = 0; p < NPT; ++p) pp[p] = page_ptr(kbase_g, j0, p);
 #pragma unroll
       for (int r = 0; r < ROUNDS; ++r)
-        lds_load16(pp[(r * 4 * KEYS_PER_LOAD) >> 4] + koff[r], kl + (r * 4 + w) * 1024);
+        lds_load16(pp[(r * NW * KEYS_PER_LOAD) >> 4] + koff[r], kl + (r * NW + w) * 1024);
     } else {
       const int slot0 = KT < psize ? (j0 & (psize - 1)) * D * 2 : 0;
 #pragma unroll
       for (int r = 0; r < ROUNDS; ++r)
-        lds_load16(page_ptr(kbase_g, j0, kpg[r]) + slot0 + koff[r], kl + (r * 4 + w) * 1024);
+        lds_load16(page_ptr(kbase_g, j0, kpg[r]) + slot0 + koff[r], kl + (r * NW + w) * 1024);
     }
   };
   auto issue_v = [&](char* vl, int j0) {
@@ -209,12 +234,12 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
       for (int p = 0; p < NPT; ++p) pp[p] = page_ptr(vbase_g, j0, p);
 #pragma unroll
       for (int r = 0; r < ROUNDS; ++r)
-        lds_load16(pp[(8 * ((r * 4 * 64) / D)) >> 4] + voff[r], vl + (r * 4 + w) * 1024);
+        lds_load16(pp[(8 * ((r * NW * 64) / D)) >> 4] + voff[r], vl + (r * NW + w) * 1024);
     } else {
       const int slot0 = KT < psize ? (j0 & (psize - 1)) * 2 : 0;
 #pragma unroll
       for (int r = 0; r < ROUNDS; ++r)
-        lds_load16(page_ptr(vbase_g, j0, vpg[r]) + slot0 + voff[r], vl + (r * 4 + w) * 1024);
+        lds_load16(page_ptr(vbase_g, j0, vpg[r]) + slot0 + voff[r], vl + (r * NW + w) * 1024);
     }
   };
   // Zero, in the V^T chunks this lane loaded itself, the keys at or past
@@ -225,9 +250,9 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
     rare_path();
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
-      const int jc = j0 + 8 * (((r * 4 + w) * 64) / D);
+      const int jc = j0 + 8 * (((r * NW + w) * 64) / D);
       if (jc + 8 > kvl) {
-        bf16x8* cp = reinterpret_cast<bf16x8*>(vl + (r * 4 + w) * 1024 + lane * 16);
+        bf16x8* cp = reinterpret_cast<bf16x8*>(vl + (r * NW + w) * 1024 + lane * 16);
         bf16x8 v = *cp;
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (jc + e >= kvl) ? (__bf16)0.0f : v[e];
@@ -245,9 +270,11 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
   const int krow = kperm(n);
   const int ksw = kswz(krow);
   const int kaddr0 = krow * NCH * 16 + 16 * (h ^ (ksw & 1)) + 32 * (ksw >> 1);
+  // this wave's dims start DW * dh into the row: whole 256-byte swizzle groups
+  const int kdh = DW * 2 * dh;
   // V^T operand of PV step t, O^T block db: row d = 32*db + n, keys
   // 16t + 8h .. +7, i.e. chunk (k8 = 2t + h, d).
-  const int vaddr0 = (h * D + n) * 16;
+  const int vaddr0 = (h * D + DW * dh + n) * 16;
   auto vaddr = [&](int t, int db) { return vaddr0 + (2 * t * D + 32 * db) * 16; };
 
   f32x16 oacc[DB];
@@ -270,7 +297,7 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
 #pragma unroll
       for (int kb = 0; kb < KBLK; ++kb)
         dst[kb] = *reinterpret_cast<const bf16x8*>(
-            kl + (kaddr0 ^ ((ks & 7) << 5)) + (ks >> 3) * 256 + kb * 32 * NCH * 16);
+            kl + (kaddr0 ^ ((ks & 7) << 5)) + (ks >> 3) * 256 + kb * 32 * NCH * 16 + kdh);
     };
 #pragma unroll
     for (int kb = 0; kb < KBLK; ++kb) s[kb] = f32x16{};
@@ -357,6 +384,27 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
     {
       f32x16 s[KBLK];
       qk(kcur, s);
+      if constexpr (DH > 1) {
+        // add the partner wave's partial scores (the other dim half); a + b
+        // is the same float in both waves, so both run identical softmaxes.
+        // The buffer is free again once every wave is past the barrier at
+        // the end of the previous step.
+#pragma unroll
+        for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            xs[w][4 * kb + c][lane] =
+                f32x4{s[kb][4 * c], s[kb][4 * c + 1], s[kb][4 * c + 2], s[kb][4 * c + 3]};
+        lds_barrier();
+#pragma unroll
+        for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const f32x4 o = xs[w ^ RG][4 * kb + c][lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[kb][4 * c + i] += o[i];
+          }
+      }
       // A tile inside every row's range of this wave needs no element mask
       // (masked tiles come back from tile_max already scaled).
       const bool full = wave_live && j0 >= k_lo && j0 + KT - 1 <= k_hi && j0 + KT - 1 <= w_pmin &&
@@ -431,7 +479,7 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
   if constexpr (SPLIT) {
     const int slot = ldu(P.items + 4 * item + 1);
     const int64_t base = ((int64_t)slot * P.num_qo_heads + head);
-    float* po = P.part_o + base * D + 4 * h;
+    float* po = P.part_o + base * D + DW * dh + 4 * h;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -439,13 +487,13 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
         f32x4 v = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
         *reinterpret_cast<f32x4*>(po + 32 * db + 8 * g) = v;
       }
-    if (h == 0) {
+    if (h == 0 && dh == 0) {
       P.part_ml[base * 2 + 0] = m_run;
       P.part_ml[base * 2 + 1] = l_tot;
     }
   } else {
     const float inv = 1.0f / l_tot;
-    const int64_t orow = ((int64_t)(q_beg + tok) * P.num_qo_heads + head) * D + 4 * h;
+    const int64_t orow = ((int64_t)(q_beg + tok) * P.num_qo_heads + head) * D + DW * dh + 4 * h;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll

@@ -86,7 +86,7 @@ int derive_tile_q(int64_t group, int64_t head_dim, int32_t* tile_q) {
   if (d != 256 && d != 512) return fail(PSW_E_UNSUPPORTED, "no prefill kernel for this head_dim");
   if (!is_pow2(g) || g > kMaxGroup)
     return fail(PSW_E_UNSUPPORTED, "GQA group must be a power of two <= 32");
-  *tile_q = kPrefillRows / g;
+  *tile_q = (d == 512 ? kPrefillRows512 : kPrefillRows) / g;
   return PSW_OK;
 }
 
