@@ -162,7 +162,7 @@ def build_rows(torch, psw, synth, dev, want):
     if "prefill_hd512" in want:
         case = synth.attention_case(3, [4096] * 4, [4096] * 4, num_pages=2048, fill_pool=False,
                                     **synth.GLOBAL)
-        # fill the pool the way serving does: the hd512 prep writes K and V
+        # fill the pool as serving does, with the hd512 prep writing K and V
         # (V = weightless norm of the raw K) from raw K ~ N(0, 0.25^2)
         pool = torch.zeros(case.pool.numel(), dtype=torch.bfloat16, device=dev)
         pd = psw.pool_desc(pool, num_layers=1, num_pages=2048, page_size=16, num_kv_heads=1,

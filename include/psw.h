@@ -9,8 +9,8 @@
  *   qkv_norm_rope_paged_prefill_hd256   fused prep: Q norm+RoPE to a contiguous
  *                                       buffer, K norm+RoPE and V weightless norm
  *                                       scattered into the layer's pool pages
- *   k_v_norm_rope_paged_prefill_hd512   fused prep: K norm+RoPE and V = weightless
- *                                       norm of the same raw K (shared inv_rms)
+ *   k_v_norm_rope_paged_prefill_hd512   fused prep: K norm+RoPE, and V = the raw K
+ *                                       normalised without weight (K's inv_rms)
  *
  * Sources (the pages this library implements):
  *   [P1] PR "feat(kernels): Rust wrapper for the hd256 windowed paged prefill",
@@ -27,16 +27,17 @@
  * Return value: PSW_OK (0) or a negative psw_status.  On any failure nothing
  * has been launched and no device memory has been written; psw_last_error()
  * returns a thread-local message naming the offending argument.  Every check
- * runs on the host before any launch ([P1] Verification: contradictory layouts,
- * out-of-range layers, page metadata past the pool, non-finite scales, lengths
- * past i32 and zero KV heads all fail as errors before any launch).
+ * runs on the host before any launch ([P1] Verification: inconsistent layouts,
+ * bad layer indices, page metadata outside the pool, non-finite scales, i32
+ * overflow and a zero KV-head count are all errors raised before launching).
  *
  * Pointers: "device" pointers are HIP device allocations owned by the caller
  * (for example torch tensors); "host" pointers are read during the call only.
  * The library never frees or retains caller memory.
  *
  * Pool layout (a whole-page, layer-indexed pool per KV family, bf16):
- *     pool[layer][page][kv][kv_head][slot][dim]     kv = 0 for K, 1 for V
+ *     K block: pool[layer][page][0][kv_head][slot][dim]
+ *     V block: pool[layer][page][1][kv_head][dim][slot]   (dim-major)
  * i.e. numel == num_layers * num_pages * 2 * num_kv_heads * page_size * head_dim
  * exactly; device offsets are 64-bit, so pools larger than 2 GiB are fine.
  *
@@ -45,11 +46,11 @@
  * (n_pages - 1) * page_size + kv_last_page_len[b].  Its qo_len =
  * qo_indptr[b+1] - qo_indptr[b] >= 1 queries are the last qo_len tokens of the
  * KV: token t sits at position start_pos + t with start_pos = kv_len - qo_len
- * ([P2] Proposed Plan: slot positions derive from start_pos + token).
+ * ([P2] Proposed Plan: a token's cache slot is its absolute position).
  *
  * Ordering: a plan records the stream it was created with; every entry point
- * rejects any other stream with PSW_E_PLAN, so pool initialisation, prep writes
- * and attention reads stay ordered without events ([P3] review thread: a fresh
+ * rejects any other stream with PSW_E_PLAN, which keeps pool setup, prep and
+ * attention in order without events ([P3] review thread: a fresh
  * stream on the same device races earlier KV writes).
  */
 #ifndef PSW_H
@@ -102,8 +103,8 @@ typedef struct {
   int64_t head_dim;
 } psw_pool;
 
-/* Host-only check of a pool descriptor (the shared checked-geometry helper that
- * both prep writes and attention reads go through, [P1] Description).  base may
+/* Host-only check of a pool descriptor (one overflow-checked geometry check
+ * used by the prep and attention entries alike, [P1] Description).  base may
  * be NULL here; entry points additionally require it non-NULL. */
 int psw_check_pool(const psw_pool* pool);
 
@@ -130,8 +131,8 @@ typedef struct {
 /* Opaque plan: validated host copy of the metadata, the recorded bounds
  * (max page id, max last-page length), the tile decision and work lists, and a
  * device mirror uploaded lazily, on the plan's stream, by the first launch that
- * needs it.  ([P1] Description: the plan records both bounds from its host
- * inputs and settles the head relation before anything divides by it.) */
+ * needs it.  ([P1] Description: the bounds are taken from the host metadata,
+ * and the query/KV head relation is validated before any division uses it.) */
 typedef struct psw_plan psw_plan;
 
 /* Creates a plan bound to `stream`.  Pure host work: no HIP call is made here,
@@ -168,8 +169,8 @@ typedef struct {
 
 int psw_plan_get_info(const psw_plan* plan, psw_plan_info* info);
 
-/* Tile-size query ([P1] Description: the plan's recorded cta_tile_q is
- * cross-checked against the kernel's own derivation).  Query tokens per prefill
+/* Tile-size query ([P1] Description: a plan tiled differently from what the
+ * kernel derives for itself is refused rather than misread).  Query tokens per prefill
  * work-group for a GQA group and head_dim; positivity is checked in the i32
  * domain. */
 int psw_prefill_tile_q(int64_t group, int64_t head_dim, int32_t* tile_q);
@@ -185,8 +186,8 @@ int psw_prefill_tile_q(int64_t group, int64_t head_dim, int32_t* tile_q);
  *   window_left: key j is visible to the query at position p iff
  *                0 <= p - j <= window_left (inclusive distance); -1 = no window
  * qo_len == 1 for every request selects the split-KV decode kernels, otherwise
- * the MFMA prefill kernel runs ([P3] Description: decode runs the prefill entry
- * at one token). */
+ * the MFMA prefill kernel runs ([P3] Description: the serving loop's decode
+ * step is a call of this entry with one query token per request). */
 int paged_prefill_window_hd256(psw_plan* plan, const psw_pool* pool, int64_t layer,
                                const void* q, float sm_scale, int64_t window_left,
                                void* o, int32_t o_dtype, psw_stream_t stream);
@@ -244,7 +245,7 @@ int psw_rope_tables(float* cos_out, float* sin_out, int64_t positions, int64_t h
 /* ----------------------------------------------------------- device check ---- */
 
 /* Second line of defence inside the prep kernels ([P2] Proposed Plan): a
- * position past the RoPE table or a page id past the pool makes the kernel skip
+ * position beyond the RoPE tables or a page id outside the pool makes it skip
  * that row's writes and record the first offending value in a per-plan device
  * word instead of trapping.  This call synchronises the plan's stream, returns
  * 0 when nothing was recorded and PSW_E_RANGE otherwise (the word is cleared). */

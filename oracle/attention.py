@@ -8,8 +8,8 @@ attention families", Description):
   query i sits at absolute position p_i = kv_len_b - qo_len_b + i, i.e.
   start_pos + i: the queries are the last qo_len_b tokens of the KV (the prep
   writes slot start_pos + token before attention reads it).  Query head h reads
-  KV head g = h // (H_q / H_kv) (the GQA group is an integer division by the KV
-  head count).  Key j is allowed for query i when
+  KV head g = h // (H_q / H_kv) (contiguous GQA groups of H_q / H_kv query
+  heads).  Key j is allowed for query i when
 
       0 <= p_i - j <= window_left      (window_left >= 0; inclusive distance)
       0 <= p_i - j                     (window_left == -1; full causal)

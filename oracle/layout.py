@@ -12,9 +12,10 @@ reading taken here, a convention and therefore parity unpinned:
 a flat bf16 buffer of exactly L * N * 2 * H_kv * P * D elements, layers outer,
 pages next.
 
-Page table.  Attention reads K/V "through a page table" whose addresses come
-from "page ids and the last-page length" (PR "feat(kernels): Rust wrapper for
-the hd256 windowed paged prefill", Description).  Reading: CSR form, request b
+Page table.  Attention finds each key through a page table: a list of page ids
+per request plus the number of filled slots in its final page (PR
+"feat(kernels): Rust wrapper for the hd256 windowed paged prefill",
+Description).  Reading: CSR form, request b
 owns ids[indptr[b]:indptr[b+1]] (at least one page) and its KV length is
 (n_pages - 1) * page_size + last_page_len with 1 <= last_page_len <= page_size.
 Logical key j of the request lives at page ids[j // P], slot j % P.

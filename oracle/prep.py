@@ -3,13 +3,13 @@
 Definitions followed (issue "gemma4: serving prep needs pool-write forms --
 hd256 QKV in one pass, hd512 V alongside K", Description and Proposed Plan):
 
-* hd256 (local layers, which carry a real v_proj): Q is normalised and rotated
-  into a contiguous output; K is normalised and rotated, and V is normalised
-  without a weight and never rotated; K and V go straight into the layer's pool
-  pages.
-* hd512 (global layers): V is the weightless norm of the same raw K the kernel
-  holds and shares K's normalising denominator; it is never rotated.  K is
-  normalised (with its weight) and rotated.
+* hd256 (local layers, which have their own V projection): Q is normalised and
+  rotated into a contiguous output; K is normalised and rotated, V is
+  normalised without a weight and not rotated; K and V are written directly
+  into the layer's pool pages.
+* hd512 (global layers): K is normalised with its weight and rotated; V is
+  the raw K normalised without a weight, reusing K's normalising denominator,
+  and is not rotated.
 * Slot contract: token t of a request lands at position start_pos + t, page
   ids[(start_pos + t) // P], slot (start_pos + t) % P, in the given layer.
 

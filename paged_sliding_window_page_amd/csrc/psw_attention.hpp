@@ -1,15 +1,15 @@
 // Paged prefill attention for gfx950: bf16 MFMA, online softmax, K/V gathered
 // through a page table.  One kernel template serves
 //   * windowed paged prefill at head_dim 256 (PR "feat(kernels): Rust wrapper
-//     for the hd256 windowed paged prefill", Description: explicit sm_scale,
-//     window_left an inclusive distance, addresses from page ids and the
-//     last-page length),
+//     for the hd256 windowed paged prefill", Description: the caller passes
+//     sm_scale, the window bound is inclusive, and key addresses follow from
+//     the page table and the length of each request's final page),
 //   * full paged prefill at head_dim 512 (PR "feat(gemma4): paged KV serving
-//     across both attention families", Description: global layers are full
-//     attention at head_dim 512 with one KV head),
-//   * the split-KV form that one-token decode runs through the same entry
-//     (same PR, Description: decode runs the prefill entry at seq_len 1), whose
-//     partial results are combined by merge_kernel.
+//     across both attention families", Description: the global family has a
+//     single KV head of 512 dims and no window),
+//   * the split-KV form used when every request of a call has one query
+//     token (same PR, Description: serving decodes through the prefill entry),
+//     whose partial results are combined by merge_kernel.
 //
 // Work-group: 4 waves, 128 query rows = (128 / group) tokens x group heads of
 // one KV head, so the group's heads share every K/V tile.  Each wave owns 32

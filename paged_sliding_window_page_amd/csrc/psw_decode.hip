@@ -1,6 +1,6 @@
 // One-token decode through the paged prefill entries (PR "feat(gemma4): paged KV
-// serving across both attention families", Description: decode runs the
-// prefill entry at seq_len 1).  Split-KV: each work-group owns one (request,
+// serving across both attention families", Description: serving decodes by
+// calling the prefill entry with one query per request).  Split-KV: each work-group owns one (request,
 // KV head, key range) unit and writes an unnormalised partial (o, running max
 // in log2 units, sum); merge_kernel combines the partials of a request.
 //

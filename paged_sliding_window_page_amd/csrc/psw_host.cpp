@@ -3,16 +3,17 @@
 //
 // Contracts implemented (see psw.h for the public statement):
 //   [P1] PR "feat(kernels): Rust wrapper for the hd256 windowed paged prefill",
-//        Description: checked geometry shared by prep writes and attention reads,
-//        checked i32 narrowing, the plan records the max page id and max
-//        last-page length and commits them only after an update fully succeeds,
-//        the head relation is settled before any division, the recorded tile is
-//        cross-checked against the kernel's own.
-//   [P1] Verification: page id past the pool, last-page length past page_size,
-//        lengths past i32 and zero KV heads all fail before launch.
-//   [P2] Proposed Plan: layer bound, whole-page pool, page coverage of
-//        [start_pos, start_pos + seq_len), position range against the RoPE
-//        tables, table lengths.
+//        Description: one overflow-checked geometry check for the prep and
+//        attention entries, checked i32 narrowing, the plan keeps the largest
+//        page id and final-page length and replaces them only when an update
+//        succeeds as a whole, query/KV heads are validated before any
+//        division, and the plan's tile must equal the kernel's own.
+//   [P1] Verification: out-of-pool page ids, final-page lengths above the
+//        page size, i32 overflow and a zero KV-head count are errors raised
+//        before any launch.
+//   [P2] Proposed Plan: the prep checks the layer index, that the pool holds
+//        whole pages, that the request's pages cover every written position,
+//        that positions stay inside the RoPE tables, and the table sizes.
 #include "psw_host.hpp"
 
 #include <algorithm>
@@ -379,7 +380,7 @@ int check_prep_call(const psw_plan* plan, const psw_pool* pool, int64_t layer,
     return fail(PSW_E_RANGE, "position " + std::to_string(s.max_kv_len - 1) +
                                  " is past the RoPE table of " + std::to_string(rope_positions) +
                                  " positions");
-  // coverage of [start_pos, start_pos + seq_len) and distinct written pages
+  // every written position has a page, and no page is written twice
   std::unordered_set<int32_t> written;
   for (int32_t b = 0; b < s.batch; ++b) {
     const int32_t qo = s.qo_indptr[b + 1] - s.qo_indptr[b];

@@ -23,8 +23,9 @@ namespace psw {
 int fail(int code, const std::string& msg);
 void clear_error();
 
-// Checked narrowing to int32 ([P1] Description: scalar narrowing goes through
-// checked conversions so a length past i32 fails instead of truncating).
+// Checked narrowing to int32 ([P1] Description: every 64-bit to 32-bit
+// conversion is checked; an overflowing length is an error, never a wrapped
+// value that happens to look legal).
 bool fits_i32(int64_t v);
 // a * b without int64 overflow; false on overflow or negative operands.
 bool checked_mul(int64_t a, int64_t b, int64_t* out);

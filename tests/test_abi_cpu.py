@@ -2,10 +2,10 @@
 every symbol the header declares, and rejects bad input before any launch.
 
 Reject contract: PR "feat(kernels): Rust wrapper for the hd256 windowed paged
-prefill", Verification (a page id past the pool, a last-page length past
-page_size, a batch length past i32 and zero KV heads fail before anything is
-launched; contradictory layouts, out-of-range layers and non-finite scales fail
-as errors) and Description (bounds committed only after an update fully
+prefill", Verification (out-of-pool page ids, final-page lengths above the
+page size, i32 overflow of batch lengths and a zero KV-head count are errors
+raised before any launch, as are inconsistent layouts, bad layer indices and
+non-finite scales) and Description (bounds committed only after an update fully
 succeeds; the plan's tile cross-checked against the kernel's).  Prep rejects:
 issue "gemma4: serving prep needs pool-write forms", Proposed Plan.
 
@@ -80,7 +80,7 @@ def test_plan_info_records_bounds():
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(kv_page_indices=[3, 4, 0]), "PSW_E_RANGE"),            # page id past the pool
+    (dict(kv_page_indices=[3, 4, 0]), "PSW_E_RANGE"),            # page id outside the pool
     (dict(kv_page_indices=[3, -1, 0]), "PSW_E_RANGE"),
     (dict(kv_last_page_len=[17, 16]), "PSW_E_RANGE"),             # past page_size
     (dict(kv_last_page_len=[0, 16]), "PSW_E_RANGE"),

@@ -179,8 +179,9 @@ def test_batch8_windowed_prefill_full_size_sampled():
 # ------------------------------------------------ hd512 full prefill ----
 
 def _global_case(seed, qo, kv, **kw):
-    """16 Q / 1 KV heads at head_dim 512; V pages = weightless RMS norm of the raw
-    K (eps 1e-6), as the global family stores them, computed by the oracle."""
+    """16 Q / 1 KV heads at head_dim 512; V pages hold the raw K normalised
+    without a weight (eps 1e-6), as the global family stores them, computed by
+    the oracle."""
     a = dict(GLOBAL)
     a.update(kw)
     case = synth.attention_case(seed, qo, kv, **a)

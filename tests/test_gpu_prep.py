@@ -2,10 +2,10 @@
 
 Contract under test (issue "gemma4: serving prep needs pool-write forms --
 hd256 QKV in one pass, hd512 V alongside K", Proposed Plan and Acceptance
-Criteria): Q against the contiguous oracle, K rotation and V weightless-norm
-placement at layout-derived offsets, the layer offset, and every region the
-kernel must never write (placement bit-exact); for hd512, V is the weightless
-norm of the raw K under the same denominator.
+Criteria): Q values against the oracle's contiguous rows, rotated K and
+weightless-normed V at the offsets the pool layout gives, the layer offset,
+and untouched memory everywhere else (placement compared bit for bit); for
+hd512, V equals the raw K normalised with K's own denominator.
 """
 import numpy as np
 import pytest
