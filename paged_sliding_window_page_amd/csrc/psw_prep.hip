@@ -79,7 +79,7 @@ __device__ __forceinline__ bool item_ok(const PrepParams& P, const Item& it) {
 }
 
 // Normalise (+ weight) and rotate one row held as two 8-element halves.
-template <int D, bool WEIGHT, bool ROTATE>
+template <bool WEIGHT, bool ROTATE>
 __device__ __forceinline__ void norm_rope(float* x1, float* x2, const float* w1, const float* w2,
                                           const float* c, const float* s, float inv) {
 #pragma unroll
@@ -99,160 +99,229 @@ __device__ __forceinline__ void norm_rope(float* x1, float* x2, const float* w1,
   }
 }
 
-// hd256: blockIdx.y selects the row kind and a group of up to 8 heads:
-// y < nqg -> Q heads 8y.., y < nqg + nkg -> K heads, else V heads.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Inputs are read once and outputs written once: streaming (non-temporal)
+// 16-byte accesses, which keep them from displacing the reused RoPE tables
+// and sustain more HBM bandwidth than cache-allocating ones.
+__device__ __forceinline__ bf16x8 load8_stream(const __bf16* p) {
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+
+__device__ __forceinline__ void widen8(bf16x8 v, float* f) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = (float)v[e];
+}
+
+__device__ __forceinline__ void store8_stream(__bf16* p, const float* f) {
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (__bf16)f[e];
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+}
+
+// 1 / sqrt(mean(x^2) + eps) over a row spread across LPR lanes
+template <int LPR>
+__device__ __forceinline__ float inv_rms(const float* x1, const float* x2, float inv_d, float eps) {
+  float ss = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
+  ss = row_sum<LPR>(ss);
+  return 1.0f / sqrtf(ss * inv_d + eps);
+}
+
+// Writes the staged V rows of `nh` heads to their dim-major V blocks: the
+// element for (head h, token t, dim d) goes to slot slot0 + t of row d.
+// vstage layout: [head][token][D + 8] bf16.  With slot0 and ntok multiples of
+// 8, each thread stores 8 consecutive slots as one 16-byte vector, and
+// consecutive threads cover consecutive 16-byte pieces of the block.
+template <int D, int THREADS>
+__device__ __forceinline__ void store_v_transposed(const PrepParams& P, const __bf16* vstage,
+                                                   const Item& it, int64_t vblock0, int nh) {
+  constexpr int RS = D + 8;
+  if ((it.slot0 & 7) == 0 && (it.ntok & 7) == 0) {
+    const int nch = it.ntok >> 3;
+    const int total = nh * D * nch;
+    for (int idx = threadIdx.x; idx < total; idx += THREADS) {
+      const int ch = idx % nch;
+      const int rest = idx / nch;
+      const int d = rest % D;
+      const int h = rest / D;
+      const __bf16* src = vstage + (h * kPrepMaxTokens + 8 * ch) * RS + d;
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = src[e * RS];
+      __bf16* dst = P.pool + vblock0 + (int64_t)h * P.ps.head + (int64_t)d * P.ps.page_size +
+                    it.slot0 + 8 * ch;
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(dst));
+    }
+  } else {
+    const int total = nh * D * it.ntok;
+    for (int idx = threadIdx.x; idx < total; idx += THREADS) {
+      const int tt = idx % it.ntok;
+      const int rest = idx / it.ntok;
+      const int d = rest % D;
+      const int h = rest / D;
+      P.pool[vblock0 + (int64_t)h * P.ps.head + (int64_t)d * P.ps.page_size + it.slot0 + tt] =
+          vstage[(h * kPrepMaxTokens + tt) * RS + d];
+    }
+  }
+}
+
+// hd256.  blockIdx.y picks the row kind and a group of up to 8 heads:
+// y < nqg -> Q heads 8y.., y < nqg + nkg -> K heads, else V heads.  Lane
+// group tt (16 lanes) owns token tt of the item and all the group's heads, so
+// the RoPE rows of its position are loaded once, and every input row of the
+// lane group is requested before the first one is used.
 __global__ __launch_bounds__(256) void prep_hd256_kernel(PrepParams P) {
-  constexpr int D = 256, LPR = 16, RPP = 256 / LPR;  // rows per pass
-  constexpr int HALF = D / 2;
-  constexpr int VSUB = 2;                            // V heads staged at a time
+  constexpr int D = 256, LPR = 16, HALF = D / 2, HG = 8;
   const Item it = read_item(P.items + kPrepItemInts * blockIdx.x);
   if (!item_ok(P, it)) return;
-  const int nqg = (P.num_qo_heads + 7) / 8;
-  const int nkg = (P.num_kv_heads + 7) / 8;
+  const int nqg = (P.num_qo_heads + HG - 1) / HG;
+  const int nkg = (P.num_kv_heads + HG - 1) / HG;
   const int y = blockIdx.y;
   const int kind = y < nqg ? 0 : (y < nqg + nkg ? 1 : 2);
   const int hg = kind == 0 ? y : (kind == 1 ? y - nqg : y - nqg - nkg);
   const int heads = kind == 0 ? P.num_qo_heads : P.num_kv_heads;
-  const int h0 = 8 * hg;
-  const int hcount = min(8, heads - h0);
+  const int h0 = HG * hg;
+  const int hcount = min(HG, heads - h0);
   const int li = threadIdx.x % LPR;
-  const int rsub = threadIdx.x / LPR;
+  const int tt = threadIdx.x / LPR;
+  const bool live = tt < it.ntok;
+  const int tok = it.tok0 + tt;
+  const int pos = it.pos0 + tt;
   const int64_t page_off = P.layer_off + (int64_t)it.page * P.ps.page;
 
+  constexpr int VST = 4;  // V heads staged per round (LDS: VST * 16 rows * 528 B)
+  __shared__ __attribute__((aligned(16))) __bf16 vstage[VST * kPrepMaxTokens * (D + 8)];
+
+  const __bf16* src = kind == 0 ? P.q_in + ((int64_t)tok * P.num_qo_heads + h0) * D
+                    : kind == 1 ? P.k_in + ((int64_t)tok * P.num_kv_heads + h0) * D
+                                : P.v_in + ((int64_t)tok * P.num_kv_heads + h0) * D;
+  bf16x8 r1[HG], r2[HG];   // raw rows, widened when used
+  if (live) {
+#pragma unroll
+    for (int h = 0; h < HG; ++h)
+      if (h < hcount) {
+        r1[h] = load8_stream(src + h * D + 8 * li);
+        r2[h] = load8_stream(src + h * D + HALF + 8 * li);
+      }
+  }
   if (kind < 2) {
-    float w1[8], w2[8];
+    float w1[8], w2[8], c[8], sn[8];
     const __bf16* wp = kind == 0 ? P.q_w : P.k_w;
     load8(wp + 8 * li, w1);
     load8(wp + HALF + 8 * li, w2);
-    const int nrows = it.ntok * hcount;
-    for (int row = rsub; row < nrows; row += RPP) {
-      const int tt = row / hcount;
-      const int hd = h0 + row - tt * hcount;
-      const int tok = it.tok0 + tt;
-      const int pos = it.pos0 + tt;
-      const __bf16* src = kind == 0 ? P.q_in + ((int64_t)tok * P.num_qo_heads + hd) * D
-                                    : P.k_in + ((int64_t)tok * P.num_kv_heads + hd) * D;
-      float x1[8], x2[8], c[8], s[8];
-      load8(src + 8 * li, x1);
-      load8(src + HALF + 8 * li, x2);
-      load8f(P.cos + (int64_t)pos * HALF + 8 * li, c);
-      load8f(P.sin + (int64_t)pos * HALF + 8 * li, s);
-      float ss = 0.0f;
+    if (!live) return;
+    load8f(P.cos + (int64_t)pos * HALF + 8 * li, c);
+    load8f(P.sin + (int64_t)pos * HALF + 8 * li, sn);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
-      ss = row_sum<LPR>(ss);
-      const float inv = 1.0f / sqrtf(ss * (1.0f / D) + P.eps);
-      norm_rope<D, true, true>(x1, x2, w1, w2, c, s, inv);
-      __bf16* dst = kind == 0 ? P.q_out + ((int64_t)tok * P.num_qo_heads + hd) * D
-                              : P.pool + page_off + (int64_t)hd * P.ps.head +
+    for (int h = 0; h < HG; ++h) {
+      if (h >= hcount) break;
+      float x1[8], x2[8];
+      widen8(r1[h], x1);
+      widen8(r2[h], x2);
+      const float inv = inv_rms<LPR>(x1, x2, 1.0f / D, P.eps);
+      norm_rope<true, true>(x1, x2, w1, w2, c, sn, inv);
+      __bf16* dst = kind == 0 ? P.q_out + ((int64_t)tok * P.num_qo_heads + h0 + h) * D
+                              : P.pool + page_off + (int64_t)(h0 + h) * P.ps.head +
                                     (int64_t)(it.slot0 + tt) * D;
-      store8(dst + 8 * li, x1);
-      store8(dst + HALF + 8 * li, x2);
+      store8_stream(dst + 8 * li, x1);
+      store8_stream(dst + HALF + 8 * li, x2);
     }
     return;
   }
 
-  // V: weightless norm, staged per VSUB heads for the transpose into the
-  // dim-major V block.  vstage: [VSUB][token][D + 2] bf16
-  __shared__ __bf16 vstage[VSUB * kPrepMaxTokens * (D + 2)];
-  for (int hs = 0; hs < hcount; hs += VSUB) {
-    const int hn = min(VSUB, hcount - hs);
-    const int nrows = it.ntok * hn;
-    for (int row = rsub; row < nrows; row += RPP) {
-      const int tt = row / hn;
-      const int hl = row - tt * hn;
-      const int tok = it.tok0 + tt;
-      const __bf16* src = P.v_in + ((int64_t)tok * P.num_kv_heads + h0 + hs + hl) * D;
-      float x1[8], x2[8];
-      load8(src + 8 * li, x1);
-      load8(src + HALF + 8 * li, x2);
-      float ss = 0.0f;
+  // V: weightless norm, staged (VST heads per round) for the transpose into
+  // the dim-major V block
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
-      ss = row_sum<LPR>(ss);
-      const float inv = 1.0f / sqrtf(ss * (1.0f / D) + P.eps);
-      __bf16* vs = vstage + (hl * kPrepMaxTokens + tt) * (D + 2);
+  for (int r = 0; r < HG / VST; ++r) {
+    if (VST * r >= hcount) break;
+    if (live) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        vs[8 * li + e] = (__bf16)(x1[e] * inv);
-        vs[HALF + 8 * li + e] = (__bf16)(x2[e] * inv);
+      for (int j = 0; j < VST; ++j) {
+        const int h = VST * r + j;
+        if (h >= hcount) break;
+        float x1[8], x2[8];
+        widen8(r1[h], x1);
+        widen8(r2[h], x2);
+        const float inv = inv_rms<LPR>(x1, x2, 1.0f / D, P.eps);
+        bf16x8 a, b;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          a[e] = (__bf16)(x1[e] * inv);
+          b[e] = (__bf16)(x2[e] * inv);
+        }
+        __bf16* vs = vstage + (j * kPrepMaxTokens + tt) * (D + 8);
+        *reinterpret_cast<bf16x8*>(vs + 8 * li) = a;
+        *reinterpret_cast<bf16x8*>(vs + HALF + 8 * li) = b;
       }
     }
     __syncthreads();
-    // consecutive threads take consecutive slots of one (head, dim) row
-    const int total = hn * D * it.ntok;
-    for (int idx = threadIdx.x; idx < total; idx += 256) {
-      const int tt = idx % it.ntok;
-      const int rest = idx / it.ntok;
-      const int d = rest % D;
-      const int hl = rest / D;
-      P.pool[page_off + P.ps.kv + (int64_t)(h0 + hs + hl) * P.ps.head +
-             (int64_t)d * P.ps.page_size + it.slot0 + tt] =
-          vstage[(hl * kPrepMaxTokens + tt) * (D + 2) + d];
-    }
+    store_v_transposed<D, 256>(P, vstage, it,
+                               page_off + P.ps.kv + (int64_t)(h0 + VST * r) * P.ps.head,
+                               min(VST, hcount - VST * r));
     __syncthreads();
   }
 }
 
 // hd512: one raw K row per (token, KV head) yields the K row (weighted norm +
-// rope) and the V row (weightless norm, same inv, no rope).
+// rope) and the V row (weightless norm, same inv, no rope).  Lane group g (32
+// lanes) owns tokens g and g + 8 of the item.
 __global__ __launch_bounds__(256) void prep_hd512_kernel(PrepParams P) {
-  constexpr int D = 512, LPR = 32, RPP = 256 / LPR;
-  constexpr int HALF = D / 2;
+  constexpr int D = 512, LPR = 32, HALF = D / 2, NG = 256 / LPR;
+  constexpr int TPG = kPrepMaxTokens / NG;  // tokens per lane group
   const Item it = read_item(P.items + kPrepItemInts * blockIdx.x);
   if (!item_ok(P, it)) return;
   const int li = threadIdx.x % LPR;
-  const int rsub = threadIdx.x / LPR;
+  const int g = threadIdx.x / LPR;
   const int heads = P.num_kv_heads;
   const int64_t page_off = P.layer_off + (int64_t)it.page * P.ps.page;
   float w1[8], w2[8];
   load8(P.k_w + 8 * li, w1);
   load8(P.k_w + HALF + 8 * li, w2);
 
-  __shared__ __bf16 vstage[kPrepMaxTokens * (D + 2)];
+  __shared__ __attribute__((aligned(16))) __bf16 vstage[kPrepMaxTokens * (D + 8)];
 
-  for (int hd0 = 0; hd0 < heads; ++hd0) {
-    for (int tt = rsub; tt < it.ntok; tt += RPP) {
-      const int tok = it.tok0 + tt;
+  for (int hd = 0; hd < heads; ++hd) {
+    bf16x8 r1[TPG], r2[TPG];
+#pragma unroll
+    for (int k = 0; k < TPG; ++k) {
+      const int tt = g + NG * k;
+      if (tt < it.ntok) {
+        const __bf16* src = P.k_in + ((int64_t)(it.tok0 + tt) * heads + hd) * D;
+        r1[k] = load8_stream(src + 8 * li);
+        r2[k] = load8_stream(src + HALF + 8 * li);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < TPG; ++k) {
+      const int tt = g + NG * k;
+      if (tt >= it.ntok) break;
       const int pos = it.pos0 + tt;
-      const __bf16* src = P.k_in + ((int64_t)tok * heads + hd0) * D;
-      float x1[8], x2[8];
-      load8(src + 8 * li, x1);
-      load8(src + HALF + 8 * li, x2);
-      float ss = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
-      ss = row_sum<LPR>(ss);
-      const float inv = 1.0f / sqrtf(ss * (1.0f / D) + P.eps);
-      float v1[8], v2[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        v1[e] = x1[e];
-        v2[e] = x2[e];
-      }
-      float c[8], s[8];
+      float c[8], sn[8];
       load8f(P.cos + (int64_t)pos * HALF + 8 * li, c);
-      load8f(P.sin + (int64_t)pos * HALF + 8 * li, s);
-      norm_rope<D, true, true>(x1, x2, w1, w2, c, s, inv);
-      __bf16* dst = P.pool + page_off + (int64_t)hd0 * P.ps.head + (int64_t)(it.slot0 + tt) * D;
-      store8(dst + 8 * li, x1);
-      store8(dst + HALF + 8 * li, x2);
-      norm_rope<D, false, false>(v1, v2, nullptr, nullptr, nullptr, nullptr, inv);
-      __bf16* vs = vstage + tt * (D + 2);
+      load8f(P.sin + (int64_t)pos * HALF + 8 * li, sn);
+      float x1[8], x2[8];
+      widen8(r1[k], x1);
+      widen8(r2[k], x2);
+      const float inv = inv_rms<LPR>(x1, x2, 1.0f / D, P.eps);
+      bf16x8 a, b;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        vs[8 * li + e] = (__bf16)v1[e];
-        vs[HALF + 8 * li + e] = (__bf16)v2[e];
+        a[e] = (__bf16)(x1[e] * inv);
+        b[e] = (__bf16)(x2[e] * inv);
       }
+      __bf16* vs = vstage + tt * (D + 8);
+      *reinterpret_cast<bf16x8*>(vs + 8 * li) = a;
+      *reinterpret_cast<bf16x8*>(vs + HALF + 8 * li) = b;
+      norm_rope<true, true>(x1, x2, w1, w2, c, sn, inv);
+      __bf16* dst = P.pool + page_off + (int64_t)hd * P.ps.head + (int64_t)(it.slot0 + tt) * D;
+      store8_stream(dst + 8 * li, x1);
+      store8_stream(dst + HALF + 8 * li, x2);
     }
     __syncthreads();
-    const int total = D * it.ntok;
-    for (int idx = threadIdx.x; idx < total; idx += 256) {
-      const int tt = idx % it.ntok;
-      const int d = idx / it.ntok;
-      P.pool[page_off + P.ps.kv + (int64_t)hd0 * P.ps.head + (int64_t)d * P.ps.page_size +
-             it.slot0 + tt] = vstage[tt * (D + 2) + d];
-    }
+    store_v_transposed<D, 256>(P, vstage, it, page_off + P.ps.kv + (int64_t)hd * P.ps.head, 1);
     __syncthreads();
   }
 }
