@@ -39,6 +39,8 @@ namespace {
 
 constexpr float kNegBig = -1.0e30f;     // finite "minus infinity" for running maxima
 constexpr float kRescaleSlack = 8.0f;   // log2 units: rescale O only past a 256x rise
+constexpr int kQkAhead = 2;  // K operand reads in flight ahead of the QK MFMAs (k-steps)
+constexpr int kPvAhead = 2;  // V^T operand reads in flight ahead of the PV MFMAs
 
 __device__ __forceinline__ int kperm(int m) {
   // S^T row m (0..31) -> key within the 32-key block.  With the 32x32 MFMA
@@ -79,6 +81,16 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt untouched
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// The value of lane l ^ 32 (the other half of the wave), through
+// v_permlane32_swap (a VALU lane swap, no LDS round trip).  Swapping x with
+// itself leaves the low half of x in both halves of one register and the high
+// half in both halves of the other, so their max is the max over l and l ^ 32.
+__device__ __forceinline__ float max_with_partner_half(float x) {
+  float lo = x, hi = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+  return fmaxf(lo, hi);
 }
 
 // Keep the compiler from if-converting a rare branch into straight-line code.
@@ -204,43 +216,64 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
     vpg[r] = (8 * k8) >> pshift;
     voff[r] = d * psize * 2 + ((8 * k8) & (psize - 1)) * 2;
   }
-  // page pointers of tile j0: pages are clamped to the request's last page
-  // (keys past kv_len are masked, and their V values zeroed after landing)
-  auto page_ptr = [&](const char* base, int j0, int p) {
-    const int idx = min((j0 >> pshift) + p, last_page);
-    return base + (int64_t)ldu(pages + idx) * page_bytes;
+  // Page ids of a tile: pages are clamped to the request's last page (keys past
+  // kv_len are masked, and their V values zeroed after landing).  With 16-slot
+  // pages the pipeline fetches the ids one step ahead with a vector load
+  // (lanes [0, NPG): the V tile's pages, lanes [NPG, 2 NPG): the K tile's)
+  // and reads them back with readlane, so issuing a tile never waits on the
+  // page table.  Other page sizes read the ids per load, through the scalar
+  // cache.
+  constexpr int NPG = KT / 8;  // most pages a tile can touch (page_size >= 8)
+  constexpr int NPP = PAGE16 ? KT / 16 : 1;
+  auto page_id = [&](int j0, int p) { return ldu(pages + min((j0 >> pshift) + p, last_page)); };
+  auto load_pids = [&](int tv, int tk) {  // tile indices of the V and K tiles
+    int r = 0;
+    if (lane < 2 * NPG) {
+      const int jt = (jt0 + (lane < NPG ? tv : tk)) * KT;
+      r = pages[min((jt >> pshift) + (lane & (NPG - 1)), last_page)];
+    }
+    return r;
   };
-  auto issue_k = [&](char* kl, int j0) {
+  // One load instruction (round r) of a K or V^T tile.  PAGE16: pp holds the
+  // base pointer of each of the tile's pages; otherwise the page is looked up
+  // per round.
+  auto k_round = [&](char* kl, const char* const* pp, auto pg, int j0, int r) {
+    const char* src;
+    if constexpr (PAGE16)
+      src = pp[(r * NW * KEYS_PER_LOAD) >> 4];
+    else
+      src = kbase_g + (int64_t)pg(kpg[r]) * page_bytes +
+            (KT < psize ? (j0 & (psize - 1)) * D * 2 : 0);
+    lds_load16(src + koff[r], kl + (r * NW + w) * 1024);
+  };
+  auto v_round = [&](char* vl, const char* const* pp, auto pg, int j0, int r) {
+    const char* src;
+    if constexpr (PAGE16)
+      src = pp[(8 * ((r * NW * 64) / D)) >> 4];
+    else
+      src = vbase_g + (int64_t)pg(vpg[r]) * page_bytes + (KT < psize ? (j0 & (psize - 1)) * 2 : 0);
+    lds_load16(src + voff[r], vl + (r * NW + w) * 1024);
+  };
+  // Copy of v made by an opaque move, issued where v's load is known to have
+  // landed: later readlanes of the copy need no wait (the compiler cannot
+  // track the load's completion across loop iterations and would otherwise
+  // wait for every load in flight).
+  auto settled = [](int v) {
+    int r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+  };
+  auto tile_pages = [&](const char* base, auto pg, const char** pp) {
     if constexpr (PAGE16) {
-      constexpr int NPT = KT / 16;
-      const char* pp[NPT];
 #pragma unroll
-      for (int p = 0; p < NPT; ++p) pp[p] = page_ptr(kbase_g, j0, p);
-#pragma unroll
-      for (int r = 0; r < ROUNDS; ++r)
-        lds_load16(pp[(r * NW * KEYS_PER_LOAD) >> 4] + koff[r], kl + (r * NW + w) * 1024);
-    } else {
-      const int slot0 = KT < psize ? (j0 & (psize - 1)) * D * 2 : 0;
-#pragma unroll
-      for (int r = 0; r < ROUNDS; ++r)
-        lds_load16(page_ptr(kbase_g, j0, kpg[r]) + slot0 + koff[r], kl + (r * NW + w) * 1024);
+      for (int p = 0; p < NPP; ++p) pp[p] = base + (int64_t)pg(p) * page_bytes;
     }
   };
-  auto issue_v = [&](char* vl, int j0) {
-    if constexpr (PAGE16) {
-      constexpr int NPT = KT / 16;
-      const char* pp[NPT];
+  auto issue_k = [&](char* kl, int j0, auto pg) {
+    const char* pp[NPP];
+    tile_pages(kbase_g, pg, pp);
 #pragma unroll
-      for (int p = 0; p < NPT; ++p) pp[p] = page_ptr(vbase_g, j0, p);
-#pragma unroll
-      for (int r = 0; r < ROUNDS; ++r)
-        lds_load16(pp[(8 * ((r * NW * 64) / D)) >> 4] + voff[r], vl + (r * NW + w) * 1024);
-    } else {
-      const int slot0 = KT < psize ? (j0 & (psize - 1)) * 2 : 0;
-#pragma unroll
-      for (int r = 0; r < ROUNDS; ++r)
-        lds_load16(page_ptr(vbase_g, j0, vpg[r]) + slot0 + voff[r], vl + (r * NW + w) * 1024);
-    }
+    for (int r = 0; r < ROUNDS; ++r) k_round(kl, pp, pg, j0, r);
   };
   // Zero, in the V^T chunks this lane loaded itself, the keys at or past
   // kv_len (their pool slots may hold anything, NaN included, and 0 * NaN would
@@ -289,41 +322,20 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
   // kept in those units.  A negative scale flips which raw score is largest.
   const float c2 = P.scale_log2;
 
-  // S^T for one tile.  K operands are read two k-steps ahead; the scheduling
-  // barrier keeps the compiler from hoisting every read.
-  auto qk = [&](const char* kl, f32x16* s) {
-    bf16x8 a[3][KBLK];
-    auto ld = [&](int ks, bf16x8* dst) {
-#pragma unroll
-      for (int kb = 0; kb < KBLK; ++kb)
-        dst[kb] = *reinterpret_cast<const bf16x8*>(
-            kl + (kaddr0 ^ ((ks & 7) << 5)) + (ks >> 3) * 256 + kb * 32 * NCH * 16 + kdh);
-    };
-#pragma unroll
-    for (int kb = 0; kb < KBLK; ++kb) s[kb] = f32x16{};
-    ld(0, a[0]);
-    ld(1, a[1]);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 2 < KS) ld(ks + 2, a[(ks + 2) % 3]);
-#pragma unroll
-      for (int kb = 0; kb < KBLK; ++kb)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks % 3][kb], qf[ks], s[kb], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
   // O^T += V^T P^T for one tile (V^T operands read two steps ahead).
-  auto pv = [&](const char* vl, const bf16x8* pb) {
+  auto pv = [&](const char* vl, const bf16x8* pb, auto extra) {
     constexpr int NSTEP = NT * DB;
-    bf16x8 a[3];
+    constexpr int RA = kPvAhead + 1;
+    bf16x8 a[RA];
     auto ld = [&](int i) { return *reinterpret_cast<const bf16x8*>(vl + vaddr(i / DB, i % DB)); };
-    a[0] = ld(0);
-    a[1] = ld(1);
+#pragma unroll
+    for (int i = 0; i < kPvAhead; ++i) a[i] = ld(i);
 #pragma unroll
     for (int i = 0; i < NSTEP; ++i) {
-      if (i + 2 < NSTEP) a[(i + 2) % 3] = ld(i + 2);
-      oacc[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % 3], pb[i / DB], oacc[i % DB],
+      if (i + kPvAhead < NSTEP) a[(i + kPvAhead) % RA] = ld(i + kPvAhead);
+      oacc[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % RA], pb[i / DB], oacc[i % DB],
                                                               0, 0, 0);
+      extra(i);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -355,94 +367,171 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
           mx = fmaxf(mx, v);
         }
     }
-    return fmaxf(mx, __shfl_xor(mx, 32));
+    return max_with_partner_half(mx);
   };
 
-  // ---- prologue: K[0], V[0] (and K[1]) resident ----
-  issue_k(k_lds0, jt0 * KT);
-  issue_v(v_lds0, jt0 * KT);
-  if (ntiles > 1) issue_k(k_lds1, (jt0 + 1) * KT);
-  __builtin_amdgcn_s_waitcnt(0);
-  sanitize(v_lds0, jt0 * KT);
-  __syncthreads();
+  // ---- pipeline ----
+  // Scores run one tile ahead of the softmax: step t computes the softmax of
+  // tile t interleaved with the QK MFMAs of tile t+1 (the VALU and the matrix
+  // unit work side by side), then O += P(t) V(t).  Tile t's K sits in K buffer
+  // t % 2 and its V^T in V buffer t % 2; the loads of K[t+2] and V[t+1] go
+  // into the buffers that K[t] and V[t-1] left, spread over the QK MFMAs, and
+  // every wave waits for its own loads at the end of the step, before the
+  // barrier that makes them visible.
+  auto qk_mfma = [&](f32x16* sacc, int ks, bf16x8 (*a)[KBLK]) {
+#pragma unroll
+    for (int kb = 0; kb < KBLK; ++kb)
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks % (kQkAhead + 1)][kb], qf[ks],
+                                                         sacc[kb], 0, 0, 0);
+  };
+  auto qk_ld = [&](const char* kl, int ks, bf16x8* dst) {
+#pragma unroll
+    for (int kb = 0; kb < KBLK; ++kb)
+      dst[kb] = *reinterpret_cast<const bf16x8*>(
+          kl + (kaddr0 ^ ((ks & 7) << 5)) + (ks >> 3) * 256 + kb * 32 * NCH * 16 + kdh);
+  };
+  // partial scores of the other dim half (head_dim 512): write, barrier, add
+  auto xs_put = [&](const f32x16* sacc) {
+    if constexpr (DH > 1) {
+#pragma unroll
+      for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          xs[w][4 * kb + c][lane] = f32x4{sacc[kb][4 * c], sacc[kb][4 * c + 1],
+                                          sacc[kb][4 * c + 2], sacc[kb][4 * c + 3]};
+    }
+  };
+  auto xs_add = [&](f32x16* sacc) {
+    // a + b is the same float in both waves of a pair, so both run identical
+    // softmaxes
+    if constexpr (DH > 1) {
+#pragma unroll
+      for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const f32x4 o = xs[w ^ RG][4 * kb + c][lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sacc[kb][4 * c + i] += o[i];
+        }
+    }
+  };
 
-  // Pipeline, iteration t (K[t] and V[t-1] resident, V[t] / K[t+1] landed or
-  // in flight):  S = Q K[t]^T;  softmax of tile t;  O += P[t-1] V[t-1];
-  // rescale O if the running max rose;  then make V[t], K[t+1] resident and
-  // start V[t+1], K[t+2].
-  // One pipeline step for tile `it`; ST is its (compile-time) buffer parity.
+  f32x16 s[KBLK];   // scores of the tile whose softmax runs next
+  int pid = 0;      // page ids of the loads of the coming step (16-slot pages)
+  {
+    // prologue: K[0], V[0], K[1] resident, S(0) computed
+    const int j0 = jt0 * KT;
+    if constexpr (PAGE16) pid = load_pids(1, 2);
+    issue_k(k_lds0, j0, [&](int p) { return page_id(j0, p); });
+    {
+      const char* pp[NPP];
+      tile_pages(vbase_g, [&](int p) { return page_id(j0, p); }, pp);
+#pragma unroll
+      for (int r = 0; r < ROUNDS; ++r)
+        v_round(v_lds0, pp, [&](int p) { return page_id(j0, p); }, j0, r);
+    }
+    if (ntiles > 1) issue_k(k_lds1, j0 + KT, [&](int p) { return page_id(j0 + KT, p); });
+    __builtin_amdgcn_s_waitcnt(0);
+    sanitize(v_lds0, j0);
+    __syncthreads();
+    if constexpr (PAGE16) pid = settled(pid);
+    bf16x8 a[kQkAhead + 1][KBLK];
+#pragma unroll
+    for (int kb = 0; kb < KBLK; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < kQkAhead; ++ks) qk_ld(k_lds0, ks, a[ks]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + kQkAhead < KS) qk_ld(k_lds0, ks + kQkAhead, a[(ks + kQkAhead) % (kQkAhead + 1)]);
+      qk_mfma(s, ks, a);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (DH > 1) {
+      xs_put(s);
+      lds_barrier();
+      xs_add(s);
+    }
+  }
+
   auto step = [&](auto ST, int it) {
     constexpr int st = decltype(ST)::value;
-    char* kcur = st ? k_lds1 : k_lds0;     // K[t]
-    char* vcur = st ? v_lds1 : v_lds0;     // V[t] (landing), later V[t+2]
-    char* vprev = st ? v_lds0 : v_lds1;    // V[t-1], then V[t+1]
+    char* kfree = st ? k_lds1 : k_lds0;   // K[t] (used) -> K[t+2]
+    char* knext = st ? k_lds0 : k_lds1;   // K[t+1]
+    char* vcur = st ? v_lds1 : v_lds0;    // V[t]
+    char* vfree = st ? v_lds0 : v_lds1;   // V[t-1] (used) -> V[t+1]
     const int j0 = (jt0 + it) * KT;
-    bf16x8 pcur[NT];
-    float lsum = 0.0f;
-    float m_new;
-    bool need;
-    {
-      f32x16 s[KBLK];
-      qk(kcur, s);
-      if constexpr (DH > 1) {
-        // add the partner wave's partial scores (the other dim half); a + b
-        // is the same float in both waves, so both run identical softmaxes.
-        // The buffer is free again once every wave is past the barrier at
-        // the end of the previous step.
+    const bool has_next = it + 1 < ntiles;
+    const bool load_v = it + 1 < ntiles;
+    const bool load_k = it + 2 < ntiles;
+    // page ids of V[t+2] and K[t+3] for the next step (16-slot pages)
+    const int pid_next = PAGE16 ? load_pids(it + 2, it + 3) : 0;
+    auto pg_v = [&](int p) { return page_id(j0 + KT, p); };
+    auto pg_k = [&](int p) { return page_id(j0 + 2 * KT, p); };
+    const char* vpp[NPP];
+    const char* kpp[NPP];
+    tile_pages(vbase_g, [&](int p) { return __builtin_amdgcn_readlane(pid, p); }, vpp);
+    tile_pages(kbase_g, [&](int p) { return __builtin_amdgcn_readlane(pid, NPG + p); }, kpp);
+
+    f32x16 s2[KBLK];   // scores of tile t+1
 #pragma unroll
-        for (int kb = 0; kb < KBLK; ++kb)
+    for (int kb = 0; kb < KBLK; ++kb) s2[kb] = f32x16{};
+    bf16x8 a[kQkAhead + 1][KBLK];
+    if (has_next) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            xs[w][4 * kb + c][lane] =
-                f32x4{s[kb][4 * c], s[kb][4 * c + 1], s[kb][4 * c + 2], s[kb][4 * c + 3]};
-        lds_barrier();
-#pragma unroll
-        for (int kb = 0; kb < KBLK; ++kb)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const f32x4 o = xs[w ^ RG][4 * kb + c][lane];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s[kb][4 * c + i] += o[i];
-          }
-      }
-      // A tile inside every row's range of this wave needs no element mask
-      // (masked tiles come back from tile_max already scaled).
-      const bool full = wave_live && j0 >= k_lo && j0 + KT - 1 <= k_hi && j0 + KT - 1 <= w_pmin &&
-                        (wl < 0 || w_pmax - j0 <= wl);
-      const float tmax = tile_max(s, !full, j0);
-      m_new = fmaxf(m_run, tmax);
-      need = __any(m_new > m_run + kRescaleSlack);
-      const float m_use = need ? m_new : m_run;
-      const float cmul = full ? c2 : 1.0f;
-      // PV of tile t-1, with the exponentials of tile t spread over its MFMAs
-      // (independent work for the VALU while the matrix unit is busy).
-      const char* vl = vprev;
-      constexpr int NSTEP = NT * DB;
-      constexpr int NE = KBLK * 16;  // exponentials per lane
-      bf16x8 a[3];
-      auto ld = [&](int i) { return *reinterpret_cast<const bf16x8*>(vl + vaddr(i / DB, i % DB)); };
-      a[0] = ld(0);
-      a[1] = ld(1);
-#pragma unroll
-      for (int i = 0; i < NSTEP; ++i) {
-        if (i + 2 < NSTEP) a[(i + 2) % 3] = ld(i + 2);
-        oacc[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % 3], pprev[i / DB],
-                                                                oacc[i % DB], 0, 0, 0);
-#pragma unroll
-        for (int e = i * NE / NSTEP; e < (i + 1) * NE / NSTEP; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], cmul, -m_use));
-          s[e >> 4][e & 15] = p;
-          lsum += p;
-          pin(p);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pcur[t][i] = (__bf16)s[t >> 1][8 * (t & 1) + i];
-      pin(lsum);
+      for (int ks = 0; ks < kQkAhead; ++ks) qk_ld(knext, ks, a[ks]);
     }
+    // the first MFMAs of QK(t+1) go out before the row max of tile t is
+    // reduced, so the matrix unit has work while the VALU does it
+    constexpr int KS0 = 4;
+    auto qk_step = [&](int ks) {
+      if (has_next) {
+        if (ks + kQkAhead < KS)
+          qk_ld(knext, ks + kQkAhead, a[(ks + kQkAhead) % (kQkAhead + 1)]);
+        qk_mfma(s2, ks, a);
+      }
+    };
+    // the loads of V[t+1] go out over the QK MFMAs, those of K[t+2] over the
+    // PV MFMAs, so the per-CU load path is busy for the whole step
+    auto load_round = [&](int ks) {
+      constexpr int PER = KS / ROUNDS;
+      if (ks % PER == 0 && load_v) v_round(vfree, vpp, pg_v, j0 + KT, ks / PER);
+    };
+#pragma unroll
+    for (int ks = 0; ks < KS0; ++ks) {
+      qk_step(ks);
+      load_round(ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // softmax of tile t: row max, running max, exponentials (spread over the
+    // remaining QK MFMAs)
+    const bool full = wave_live && j0 >= k_lo && j0 + KT - 1 <= k_hi && j0 + KT - 1 <= w_pmin &&
+                      (wl < 0 || w_pmax - j0 <= wl);
+    const float tmax = tile_max(s, !full, j0);
+    const float m_new = fmaxf(m_run, tmax);
+    const bool need = __any(m_new > m_run + kRescaleSlack);
+    const float m_use = need ? m_new : m_run;
+    const float cmul = full ? c2 : 1.0f;
+    float lsum = 0.0f;
+    constexpr int NE = KBLK * 16;  // exponentials per lane
+#pragma unroll
+    for (int ks = KS0; ks < KS; ++ks) {
+      qk_step(ks);
+      load_round(ks);
+#pragma unroll
+      for (int e = (ks - KS0) * NE / (KS - KS0); e < (ks - KS0 + 1) * NE / (KS - KS0); ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], cmul, -m_use));
+        s[e >> 4][e & 15] = p;
+        lsum += p;
+        pin(p);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bf16x8 pb[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[t][i] = (__bf16)s[t >> 1][8 * (t & 1) + i];
+    pin(lsum);
     if (need) {
       rare_path();
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -452,18 +541,23 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
       for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
     }
     l_run += lsum;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) pprev[t] = pcur[t];
-
-    // make V[t] and K[t+1] resident; the buffers of K[t] and V[t-1] are free
-    // once every wave is past this barrier
+    // O += P(t) V(t)
+    pv(vcur, pb, [&](int i) {
+      constexpr int PER = NT * DB / ROUNDS;
+      if (i % PER == 0 && load_k) k_round(kfree, kpp, pg_k, j0 + 2 * KT, i / PER);
+    });
+    // hand over: tile t+1's partial scores to the partner wave (after every
+    // wave has read the previous ones), this wave's loads landed and zeroed
+    // past kv_len, then the barrier
+    if constexpr (DH > 1) lds_barrier();
+    xs_put(s2);
     __builtin_amdgcn_s_waitcnt(0);
-    if (it >= 1) sanitize(vcur, j0);
+    if (load_v) sanitize(vfree, j0 + KT);
     __syncthreads();
-    if (it + 1 < ntiles) {
-      issue_v(vprev, j0 + KT);
-      if (it + 2 < ntiles) issue_k(kcur, j0 + 2 * KT);
-    }
+    xs_add(s2);
+#pragma unroll
+    for (int kb = 0; kb < KBLK; ++kb) s[kb] = s2[kb];
+    if constexpr (PAGE16) pid = settled(pid_next);
   };
   int it = 0;
   for (; it + 1 < ntiles; it += 2) {
@@ -471,7 +565,6 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
     step(std::integral_constant<int, 1>{}, it + 1);
   }
   if (it < ntiles) step(std::integral_constant<int, 0>{}, it);
-  pv(((ntiles - 1) & 1) ? v_lds1 : v_lds0, pprev);
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!row_valid) return;
