@@ -2,6 +2,7 @@
 // head_dim is its own translation unit so that it can be compiled with the
 // code-generation options that suit its register budget.
 #include "psw_attention.hpp"
+#include "psw_prefill_pp.hpp"
 
 namespace psw_dev {
 namespace {
@@ -9,6 +10,14 @@ namespace {
 template <bool SPLIT, bool OB>
 hipError_t launch_one(const AttnParams& p, int n_items, hipStream_t s) {
   const dim3 grid(n_items * p.num_kv_heads);
+  if constexpr (!SPLIT) {
+    // prefill: the two-group ping-pong kernel, 256 query rows per work-group
+    if (p.ps.page_size == 16)
+      hipLaunchKernelGGL((prefill256_pp_kernel<OB, true>), grid, dim3(512), 0, s, p);
+    else
+      hipLaunchKernelGGL((prefill256_pp_kernel<OB, false>), grid, dim3(512), 0, s, p);
+    return hipGetLastError();
+  }
   if (p.ps.page_size == 16)
     hipLaunchKernelGGL((attention_kernel<256, SPLIT, OB, true>), grid, dim3(256), 0, s, p);
   else

@@ -38,7 +38,7 @@ int check_pool(const psw_pool* pool, bool need_base);
 
 // Tiling decisions, shared by the plan (which records them) and the device
 // code (which was compiled for them).
-constexpr int kPrefillRows = 128;          // query rows (token x head) per work-group
+constexpr int kPrefillRows = 256;          // query rows (token x head) per work-group (head_dim 256)
 constexpr int kPrefillRows512 = 64;        // the same at head_dim 512 (dims split over wave pairs)
 constexpr int kKvTile256 = 64;             // keys per prefill tile at head_dim 256
 constexpr int kKvTile512 = 32;             // keys per prefill tile at head_dim 512

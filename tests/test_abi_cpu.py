@@ -76,7 +76,7 @@ def test_plan_info_records_bounds():
     assert info["batch"] == 2 and info["total_qo"] == 9 and info["total_pages"] == 3
     assert info["max_page_id"] == 3 and info["max_last_page_len"] == 16
     assert info["max_kv_len"] == 20 and info["max_qo_len"] == 5
-    assert info["group"] == 2 and info["tile_q"] == 64 and info["generation"] == 1
+    assert info["group"] == 2 and info["tile_q"] == 128 and info["generation"] == 1
 
 
 @pytest.mark.parametrize("over,status", [
@@ -117,9 +117,9 @@ def test_kv_len_past_i32_fails():
 
 
 def test_tile_query_checks_in_i32_domain():
-    assert psw.prefill_tile_q(2, 256) == 64
+    assert psw.prefill_tile_q(2, 256) == 128
     assert psw.prefill_tile_q(16, 512) == 4
-    assert psw.prefill_tile_q(1, 256) == 128
+    assert psw.prefill_tile_q(1, 256) == 256
     assert _code(lambda: psw.prefill_tile_q(2 ** 32 + 2, 256)) == "PSW_E_OVERFLOW"
     assert _code(lambda: psw.prefill_tile_q(0, 256)) == "PSW_E_HEADS"
     assert _code(lambda: psw.prefill_tile_q(-4, 256)) == "PSW_E_HEADS"
