@@ -8,6 +8,8 @@
 // V^T [32 keys][256 dims], 16 KiB each, three buffers each in LDS), shared by
 // all 256 rows.  Each wave keeps Q dims 0..127 of its rows in registers and
 // dims 128..255 in LDS (64 KiB), which leaves room for two waves per SIMD.
+// Q arrives through LDS (whole rows per load instruction, then read back in
+// the MFMA operand layout) and O leaves through LDS (whole rows per store).
 //
 // A wave alternates two kinds of phase:
 //   MFMA phase u:  O += P(u-1) V(u-1);  S(u) = K(u) Q^T         (32 MFMAs)
@@ -20,11 +22,12 @@
 // rows read in the kperm order, dim-major V^T chunks), so P^T feeds the PV
 // MFMAs straight from the S^T accumulators.
 //
-// Loads: group 0's ALU phase u loads K(u+2) and V(u+1) whole (8 load
-// instructions per wave) into the buffers K(u-1) and V(u-2) left, waits for
-// the loads of its previous ALU phase (vmcnt(8)), zeroes V(u)'s keys past
-// kv_len in the chunks it loaded, and the barrier that follows publishes
-// them: every tile is resident one full phase before its first reader.
+// Loads are split between the groups so that each ALU phase issues four load
+// instructions per wave: group 0's ALU phase u loads K(u+2) into the buffer
+// K(u-1) left, group 1's loads V(u+2) into the buffer of V(u-1); each waits
+// for the loads of its own previous ALU phase (vmcnt(4)), group 1 zeroes the
+// keys past kv_len of the V tile that just landed, and the barrier that
+// follows publishes the tile, at least one phase before its first reader.
 #pragma once
 #include "psw_attention.hpp"
 
@@ -44,6 +47,16 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, const char* lds_dst)
                : "memory", "m0");
 }
 
+// The same with a wave-uniform 64-bit base and a 32-bit per-lane offset (the
+// saddr form), which keeps one VGPR per address instead of two.
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, const char* lds_dst) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_dst;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+
 template <bool OUT_BF16, bool PAGE16>
 __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   constexpr int D = 256;
@@ -54,7 +67,6 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   constexpr int KS = D / 16;       // QK k-steps
   constexpr int TILE = KT * D * 2; // 16 KiB
   constexpr int NW = 8;
-  constexpr int LPW = 2;           // load instructions per wave per tile half (K, and V)
   constexpr int AH = 2;            // LDS operand reads in flight ahead of the MFMAs
 
   __shared__ __attribute__((aligned(1024))) char kb0[TILE];
@@ -114,19 +126,16 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   const int w_pmax = start + min(wt0 + tok_w, qo_len) - 1;
   const bool wave_live = wt0 < qo_len;
 
+  // Q rows of this wave in LDS, in halves of 128 dims: [row n][16 chunks of
+  // 16 B], chunk c of row n stored at position c ^ (n % 16), so that the 16
+  // rows a ds_read_b128 serves together fall in distinct banks.  Dims
+  // 128..255 stay in qlds; dims 0..127 pass through a tile buffer that is not
+  // in use yet on their way to registers.
   bf16x8 qf[KSR];
-  char* const qw = qlds + w * (KS - KSR) * 1024 + lane * 16;  // this lane's Q chunks in LDS
-  {
-    const __bf16* qrow =
-        P.q + ((int64_t)(q_beg + (row_valid ? tok : 0)) * P.num_qo_heads + head) * D + 8 * h;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
-      v = row_valid ? v : bf16x8{};
-      if (ks < KSR) qf[ks] = v;
-      else *reinterpret_cast<bf16x8*>(qw + (ks - KSR) * 1024) = v;
-    }
-  }
+  char* const qhi = qlds + w * 8192;
+  char* const qlo = ((w >> 1) == 0 ? kb2 : (w >> 1) == 1 ? vb0 : (w >> 1) == 2 ? vb1 : vb2) +
+                    (w & 1) * 8192;
+  const int qrd = n * 256 + ((h ^ (n & 15)) << 4);  // k-step ks of the half: qrd ^ (ks << 5)
 
   const char* kbase_g =
       reinterpret_cast<const char*>(P.pool + P.layer_off + (int64_t)kvh * P.ps.head);
@@ -143,9 +152,6 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   // Group g loads instructions 8 g .. 8 g + 7 (keys 16 g .. 16 g + 15), wave
   // wg of the group instructions 8 g + 4 r + wg, r < LPW.
   auto page_id = [&](int idx) __attribute__((always_inline)) { return ldu(pages + min(idx, last_page)); };
-
-
-
 
   // ---- LDS operand addresses (as in attention_kernel, 32-key tiles) ----
   const int krow = kperm(n);
@@ -190,7 +196,8 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
       // on the same schedule
       bf16x8 a[AH + 1], qa[AH + 1];
       auto ld = [&](int ks) __attribute__((always_inline)) {
-        if (ks >= KSR) qa[ks % (AH + 1)] = *reinterpret_cast<const bf16x8*>(qw + (ks - KSR) * 1024);
+        if (ks >= KSR)
+          qa[ks % (AH + 1)] = *reinterpret_cast<const bf16x8*>(qhi + (qrd ^ ((ks - KSR) << 5)));
         a[ks % (AH + 1)] =
             *reinterpret_cast<const bf16x8*>(kl + (kaddr0 ^ ((ks & 7) << 5)) + (ks >> 3) * 256);
       };
@@ -258,74 +265,30 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
     l_run += lsum;
   };
 
-  // ---- prologue: K(0), K(1), V(0) resident ----
-  {
-    const int j0 = jt0 * KT;
-    // all 16 instructions of each tile, two per wave
-    auto all_k = [&](char* kl, int jj) __attribute__((always_inline)) {
-#pragma unroll
-      for (int r = 0; r < LPW; ++r) {
-        const int ins = 2 * w + r;  // 0..15
-        const int u = ins * 64 + lane;
-        const int key = u / NCH;
-        const int c = (u % NCH) ^ kswz(key);
-        const int keyg = jj + key;
-        const int64_t pg = page_id(keyg >> pshift);
-        lds_dma16(kbase_g + pg * page_bytes + (int64_t)(keyg & (psize - 1)) * D * 2 + c * 16,
-                   kl + ins * 1024);
-      }
-    };
-    auto all_v = [&](char* vl, int jj) __attribute__((always_inline)) {
-#pragma unroll
-      for (int r = 0; r < LPW; ++r) {
-        const int ins = 2 * w + r;
-        const int keyg = jj + 8 * (ins >> 2);
-        const int d = 64 * (ins & 3) + lane;
-        const int64_t pg = page_id(keyg >> pshift);
-        lds_dma16(vbase_g + pg * page_bytes + (int64_t)d * psize * 2 + (keyg & (psize - 1)) * 2,
-                   vl + ins * 1024);
-      }
-    };
-    all_k(kb0, j0);
-    all_k(kb1, j0 + KT);
-    all_v(vb0, j0);
-    __builtin_amdgcn_s_waitcnt(0);
-    // zero V(0)'s keys past kv_len in the chunks this wave loaded
-    if (j0 + KT > kvl) {
-      rare_path();
-#pragma unroll
-      for (int r = 0; r < LPW; ++r) {
-        const int ins = 2 * w + r;
-        const int jc = j0 + 8 * (ins >> 2);
-        if (jc + 8 > kvl) {
-          bf16x8* cp = reinterpret_cast<bf16x8*>(vb0 + ins * 1024 + lane * 16);
-          bf16x8 v = *cp;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (jc + e >= kvl) ? (__bf16)0.0f : v[e];
-          *cp = v;
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  // Tile loads are issued by group 0 only, in its ALU phases: ALU(j) loads
-  // K(j+2) and V(j+1) whole (8 instructions per wave), waits for the loads
-  // of ALU(j-1) and zeroes V(j) past kv_len.  The page ids are read through
-  // the scalar cache at the start of the ALU phase before.
-  int64_t kpid[2] = {0, 0}, vpid[2] = {0, 0};
-  auto fetch_pids = [&](int k_tile, int v_tile, int64_t* kp, int64_t* vp)
-                        __attribute__((always_inline)) {
+  // Tile loads, in the ALU phases: group 0's ALU(j) loads K(j+2), group 1's
+  // V(j+2) (ALU(-1) of group 1 also V(0)), four instructions per wave; each
+  // then waits for its loads of ALU(j-1), and group 1 zeroes the keys past
+  // kv_len of V(j+1).  With 16-slot pages the page ids of a tile are read
+  // through the scalar cache one ALU phase before its loads.
+  int64_t tpid[2] = {0, 0};  // page ids of this wave's next tile
+  auto fetch_pids = [&](int tile, int64_t* tp) __attribute__((always_inline)) {
     if constexpr (PAGE16) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        kp[p] = page_id(((jt0 + k_tile) * KT >> 4) + p);
-        vp[p] = page_id(((jt0 + v_tile) * KT >> 4) + p);
-      }
+      for (int p = 0; p < 2; ++p) tp[p] = page_id(((jt0 + tile) * KT >> 4) + p);
     }
   };
-  // the 16 instructions of a tile, four per wave of group 0
+  // the 16 instructions of a tile, four per wave of the loading group
   auto k_tile_load = [&](char* kl, int jj, const int64_t* kp) __attribute__((always_inline)) {
+    if constexpr (PAGE16) {
+      // instruction 4 r + wg: key 8 r + 2 wg + h (page r / 2), chunk n ^ kswz(key)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = 8 * (r & 1) + 2 * wg + h;
+        const uint32_t off = key * D * 2 + ((n ^ kswz(key)) << 4);
+        lds_dma16_s(kbase_g + kp[r >> 1] * page_bytes, off, kl + (4 * r + wg) * 1024);
+      }
+      return;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int ins = 4 * r + wg;
@@ -339,6 +302,14 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
     }
   };
   auto v_tile_load = [&](char* vl, int jj, const int64_t* vp) __attribute__((always_inline)) {
+    if constexpr (PAGE16) {
+      // instruction 4 r + wg: keys 8 r .. 8 r + 7 (page r / 2), dim 64 wg + lane
+      const uint32_t off = (64 * wg + lane) * 32;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        lds_dma16_s(vbase_g + vp[r >> 1] * page_bytes + 16 * (r & 1), off, vl + (4 * r + wg) * 1024);
+      return;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int ins = 4 * r + wg;
@@ -366,27 +337,54 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
     }
   };
 
-  // ALU(j): softmax of S(j) (if j is a tile), group 0's loads, barrier.
-  // KB/VB: buffers of K(j+2), V(j+1); VP: buffer of V(j).
-  auto alu_phase = [&](int j, int KB, int VB, int VP) __attribute__((always_inline)) {
-    int64_t kn[2] = {0, 0}, vn[2] = {0, 0};
+  // ---- prologue: K(0) (group 0) and K(1) (group 1), then Q ----
+  {
+    int64_t p0[2] = {0, 0};
+    fetch_pids(grp, p0);
+    k_tile_load(grp == 0 ? kb0 : kb1, (jt0 + grp) * KT, p0);
+    // 8 instructions per half, each 4 whole half-rows (16 lanes per row);
+    // rows past qo_len read the last row of the request (never stored)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 4 * i + (lane >> 4);
+      const int c = (lane & 15) ^ (row & 15);
+      const int t = min(t0 + w * tok_w + (row >> gs), qo_len - 1);
+      const int hd = (kvh << gs) + (row & ((1 << gs) - 1));
+      const char* g = reinterpret_cast<const char*>(
+                          P.q + ((int64_t)(q_beg + t) * P.num_qo_heads + hd) * D) + c * 16;
+      lds_dma16(g, qlo + i * 1024);
+      lds_dma16(g + 256, qhi + i * 1024);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int ks = 0; ks < KSR; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qlo + (qrd ^ (ks << 5)));
+    // K(0), K(1) and every wave's Q landed; the Q scratch halves are read
+    lds_barrier();
+  }
+
+  // ALU(j): this group's loads, softmax of S(j) (if j is a tile), barrier.
+  auto alu_phase = [&](int j) __attribute__((always_inline)) {
+    int64_t tn[2] = {0, 0};
+    fetch_pids(j + 3, tn);
     if (grp == 0) {
-      fetch_pids(j + 3, j + 2, kn, vn);
-      k_tile_load(kbuf(KB), (jt0 + j + 2) * KT, kpid);
-      v_tile_load(vbuf(VB), (jt0 + j + 1) * KT, vpid);
+      k_tile_load(kbuf(j + 2), (jt0 + j + 2) * KT, tpid);
+    } else {
+      if (j < 0) {
+        rare_path();
+        int64_t p0[2] = {0, 0};
+        fetch_pids(0, p0);
+        v_tile_load(vbuf(0), jt0 * KT, p0);
+      }
+      v_tile_load(vbuf(j + 2), (jt0 + j + 2) * KT, tpid);
     }
     if (j >= 0 && j < ntiles) softmax((jt0 + j) * KT);
-    if (grp == 0) {
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(8 | 0x70 | 0xF00);  // vmcnt(8): ALU(j-1)'s loads landed
-      asm volatile("" ::: "memory");
-      v_tile_sanitize(vbuf(VP), (jt0 + j) * KT);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(4 | 0x70 | 0xF00);  // vmcnt(4): ALU(j-1)'s loads landed
+    asm volatile("" ::: "memory");
+    if (grp == 1) v_tile_sanitize(vbuf(j + 1), (jt0 + j + 1) * KT);
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        kpid[p] = kn[p];
-        vpid[p] = vn[p];
-      }
-    }
+    for (int p = 0; p < 2; ++p) tpid[p] = tn[p];
     lds_barrier();
   };
   // MFMA(u): PV(u-1) from V(u-1), QK(u) from K(u)
@@ -396,36 +394,65 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   };
   // loop body u >= 1 (compile-time u % 3 picks the buffers)
 
-  fetch_pids(2, 1, kpid, vpid);
-  // group 1 runs an empty ALU(-1) first; group 0 starts with MFMA(0)
+  fetch_pids(grp == 0 ? 2 : 1, tpid);
+  // group 1 starts with ALU(-1) (no softmax, the first V loads); group 0
+  // with MFMA(0)
   for (int u = 0; u <= ntiles; ++u) {
-    if (grp == 1 || u > 0) alu_phase(u - 1, u + 1, u, u + 2);
+    if (grp == 1 || u > 0) alu_phase(u - 1);
     mfma_phase_t(u, u, u + 2);
   }
   // tail: group 0 matches group 1's extra lead-in barrier
   if (grp == 0) lds_barrier();
-  // no tile loads in flight past this point
+  // every wave's tile loads landed: all of LDS is free
   __builtin_amdgcn_s_waitcnt(0);
+  lds_barrier();
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!row_valid) return;
   const float inv = 1.0f / l_tot;
-  const int64_t orow = ((int64_t)(q_beg + tok) * P.num_qo_heads + head) * D + 4 * h;
+  if constexpr (OUT_BF16) {
+    // O rows of this wave through 16 KiB of LDS: [row n][32 chunks of 16 B],
+    // chunk c of row n at position c ^ n; then two whole rows per store
+    char* const stg = w < 6 ? ((w >> 1) == 0 ? (w & 1 ? kb1 : kb0)
+                               : (w >> 1) == 1 ? (w & 1 ? vb0 : kb2) : (w & 1 ? vb2 : vb1))
+                            : qlds + (w - 6) * 16384;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int off = 32 * db + 8 * g;
-      if constexpr (OUT_BF16) {
+      for (int g = 0; g < 4; ++g) {
         bf16x4 v = {(__bf16)(oacc[db][4 * g] * inv), (__bf16)(oacc[db][4 * g + 1] * inv),
                     (__bf16)(oacc[db][4 * g + 2] * inv), (__bf16)(oacc[db][4 * g + 3] * inv)};
-        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(P.o) + orow + off) = v;
-      } else {
+        *reinterpret_cast<bf16x4*>(stg + n * 512 + (((4 * db + g) ^ n) << 4) + 8 * h) = v;
+      }
+    // LDS operations of one wave complete in order: no wait between the
+    // writes above and the reads below, only no compiler reordering
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    const int c = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 2 * i + (lane >> 5);
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(stg + r * 512 + ((c ^ r) << 4));
+      const int t = t0 + w * tok_w + (r >> gs);
+      if (t < qo_len) {
+        const int hd = (kvh << gs) + (r & ((1 << gs) - 1));
+        *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(P.o) +
+                                   ((int64_t)(q_beg + t) * P.num_qo_heads + hd) * D + c * 8) = v;
+      }
+    }
+  } else {
+    if (!row_valid) return;
+    const int64_t orow = ((int64_t)(q_beg + tok) * P.num_qo_heads + head) * D + 4 * h;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int off = 32 * db + 8 * g;
         f32x4 v = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
                    oacc[db][4 * g + 3] * inv};
         *reinterpret_cast<f32x4*>(static_cast<float*>(P.o) + orow + off) = v;
       }
-    }
+  }
 }
 
 }  // namespace
