@@ -149,8 +149,7 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   // ---- tile loads ----
   // A tile is 16 load instructions of 1 KiB; instruction `ins` covers K keys
   // 2 ins, 2 ins + 1 and V^T chunks (k8 = ins / 4, d = 64 (ins % 4) + lane).
-  // Group g loads instructions 8 g .. 8 g + 7 (keys 16 g .. 16 g + 15), wave
-  // wg of the group instructions 8 g + 4 r + wg, r < LPW.
+  // Wave wg of the loading group issues instructions 4 r + wg, r < 4.
   auto page_id = [&](int idx) __attribute__((always_inline)) { return ldu(pages + min(idx, last_page)); };
 
   // ---- LDS operand addresses (as in attention_kernel, 32-key tiles) ----
