@@ -57,6 +57,14 @@ __device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, co
                : "memory", "m0");
 }
 
+// A copy of v the compiler cannot see through (values derived from it are
+// recomputed where they are used instead of being held in registers).
+__device__ __forceinline__ int opaque(int v) {
+  int r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+  return r;
+}
+
 template <bool OUT_BF16, bool PAGE16>
 __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   constexpr int D = 256;
@@ -67,7 +75,7 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   constexpr int KS = D / 16;       // QK k-steps
   constexpr int TILE = KT * D * 2; // 16 KiB
   constexpr int NW = 8;
-  constexpr int AH = 2;            // LDS operand reads in flight ahead of the MFMAs
+  constexpr int AH = 3;            // LDS operand reads in flight ahead of the MFMAs
 
   __shared__ __attribute__((aligned(1024))) char kb0[TILE];
   __shared__ __attribute__((aligned(1024))) char kb1[TILE];
@@ -169,48 +177,56 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) pb[t] = bf16x8{};
 
-  // MFMA phase: PV of the previous tile (if any), then QK of this one (if any);
-  // LDS operand reads run AH MFMAs ahead.
-  auto mfma_phase = [&](const char* vl, bool do_pv, const char* kl, bool do_qk) __attribute__((always_inline)) {
-    if (do_pv) {
-      constexpr int NV = NT * DB;
-      bf16x8 a[AH + 1];
-      // O block db takes its NT MFMAs back to back
-      auto ld = [&](int i) __attribute__((always_inline)) {
-        const int t = i % NT, db = i / NT;
-        return *reinterpret_cast<const bf16x8*>(vl + vaddr0 + (2 * t * D + 32 * db) * 16);
-      };
-#pragma unroll
-      for (int i = 0; i < AH; ++i) a[i] = ld(i);
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        if (i + AH < NV) a[(i + AH) % (AH + 1)] = ld(i + AH);
-        oacc[i / NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % (AH + 1)], pb[i % NT],
-                                                                oacc[i / NT], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+  // MFMA phase: PV of the previous tile (ops 0..NV-1, if any), then QK of
+  // this one (if any), as one sequence of ops whose LDS operand reads run AH
+  // ops ahead through a ring of registers.  The first AH reads are issued at
+  // the end of the phase before (preload), so the phase opens with an MFMA.
+  // The swizzled offsets are formed from opaque copies where they are used,
+  // not kept in registers across the loop.
+  constexpr int NV = NT * DB;
+  bf16x8 ra[AH + 1];  // A operands: V^T chunks (PV ops), K chunks (QK ops)
+  bf16x8 rq[AH + 1];  // B operands of the QK ops whose Q part sits in LDS
+  auto load_op = [&](int i, auto pv_c, auto qk_c, const char* vl, const char* kl, int ka, int qb)
+                     __attribute__((always_inline)) {
+    constexpr bool PV = decltype(pv_c)::value;
+    if (PV && i < NV) {
+      const int t = i % NT, db = i / NT;  // O block db takes its NT MFMAs back to back
+      ra[i % (AH + 1)] = *reinterpret_cast<const bf16x8*>(vl + vaddr0 + (2 * t * D + 32 * db) * 16);
+    } else {
+      const int ks = PV ? i - NV : i;
+      if (ks >= KSR)
+        rq[i % (AH + 1)] = *reinterpret_cast<const bf16x8*>(qhi + (qb ^ ((ks - KSR) << 5)));
+      ra[i % (AH + 1)] =
+          *reinterpret_cast<const bf16x8*>(kl + (ka ^ ((ks & 7) << 5)) + (ks >> 3) * 256);
     }
-    if (do_qk) {
-      // K operands AH k-steps ahead; Q operands of the upper k-steps from LDS
-      // on the same schedule
-      bf16x8 a[AH + 1], qa[AH + 1];
-      auto ld = [&](int ks) __attribute__((always_inline)) {
-        if (ks >= KSR)
-          qa[ks % (AH + 1)] = *reinterpret_cast<const bf16x8*>(qhi + (qrd ^ ((ks - KSR) << 5)));
-        a[ks % (AH + 1)] =
-            *reinterpret_cast<const bf16x8*>(kl + (kaddr0 ^ ((ks & 7) << 5)) + (ks >> 3) * 256);
-      };
+  };
+  auto preload = [&](auto pv_c, const char* vl, const char* kl) __attribute__((always_inline)) {
+    const int ka = opaque(kaddr0), qb = opaque(qrd);
 #pragma unroll
-      for (int i = 0; i < AH; ++i) ld(i);
-      s = f32x16{};
+    for (int i = 0; i < AH; ++i) load_op(i, pv_c, std::true_type{}, vl, kl, ka, qb);
+  };
+  auto mfma_seq = [&](auto pv_c, auto qk_c, const char* vl, const char* kl) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(pv_c)::value, QK = decltype(qk_c)::value;
+    constexpr int NOP = (PV ? NV : 0) + (QK ? KS : 0);
+    const int ka = opaque(kaddr0), qb = opaque(qrd);
+    // the preloaded operands and P pass through an empty statement that stays
+    // after the barrier, so no MFMA of this phase is hoisted above it
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + AH < KS) ld(ks + AH);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks % (AH + 1)],
-                                                    ks < KSR ? qf[ks] : qa[ks % (AH + 1)], s, 0,
-                                                    0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < AH; ++i) asm volatile("" : "+v"(ra[i]));
+    if (PV) asm volatile("" : "+v"(pb[0]), "+v"(pb[1]));
+    if (QK) s = f32x16{};
+#pragma unroll
+    for (int i = 0; i < NOP; ++i) {
+      if (i + AH < NOP) load_op(i + AH, pv_c, qk_c, vl, kl, ka, qb);
+      if (PV && i < NV) {
+        oacc[i / NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[i % (AH + 1)], pb[i % NT],
+                                                                oacc[i / NT], 0, 0, 0);
+      } else {
+        const int ks = PV ? i - NV : i;
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[i % (AH + 1)],
+                                                    ks < KSR ? qf[ks] : rq[i % (AH + 1)], s, 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -221,13 +237,17 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
                       (wl < 0 || w_pmax - j0 <= wl);
     float mx = -__builtin_inff();
     if (full) {
-      float hi = -__builtin_inff(), lo = __builtin_inff();
+      // max of s * c2: c2 times the max of s, or of the min for a negative c2
+      float e = s[0];
+      if (c2 >= 0.0f) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        hi = fmaxf(hi, s[r]);
-        lo = fminf(lo, s[r]);
+        for (int r = 1; r < 16; ++r) e = fmaxf(e, s[r]);
+      } else {
+        rare_path();
+#pragma unroll
+        for (int r = 1; r < 16; ++r) e = fminf(e, s[r]);
       }
-      mx = c2 >= 0.0f ? hi * c2 : lo * c2;
+      mx = e * c2;
     } else {
       rare_path();
       // register r holds key j0 + 16 (r / 8) + 8 h + r % 8
@@ -262,6 +282,9 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
       for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
     }
     l_run += lsum;
+    // P(t) complete here, inside the ALU phase: keep the compiler from
+    // sinking the exponentials into the next MFMA phase
+    asm volatile("" ::"v"(pb[0]), "v"(pb[1]));
   };
 
   // Tile loads, in the ALU phases: group 0's ALU(j) loads K(j+2), group 1's
@@ -276,47 +299,40 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
       for (int p = 0; p < 2; ++p) tp[p] = page_id(((jt0 + tile) * KT >> 4) + p);
     }
   };
-  // the 16 instructions of a tile, four per wave of the loading group
-  auto k_tile_load = [&](char* kl, int jj, const int64_t* kp) __attribute__((always_inline)) {
+  // One load instruction r (0..3) of wave wg of the loading group: K rows
+  // and V^T chunks of instruction 4 r + wg of the tile (16 instructions of
+  // 1 KiB per tile).  kp / vp: the tile's two page ids (16-slot pages).
+  auto k_load = [&](char* kl, int jj, const int64_t* kp, int r) __attribute__((always_inline)) {
     if constexpr (PAGE16) {
-      // instruction 4 r + wg: key 8 r + 2 wg + h (page r / 2), chunk n ^ kswz(key)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = 8 * (r & 1) + 2 * wg + h;
-        const uint32_t off = key * D * 2 + ((n ^ kswz(key)) << 4);
-        lds_dma16_s(kbase_g + kp[r >> 1] * page_bytes, off, kl + (4 * r + wg) * 1024);
-      }
-      return;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
+      // key 8 r + 2 wg + h of the tile (page r / 2), chunk n ^ kswz(key);
+      // the lane offsets are recomputed at each use (registers are scarce)
+      const int ln = opaque(lane);
+      const int key = 8 * (r & 1) + 2 * wg + (ln >> 5);
+      const uint32_t off = key * D * 2 + (((ln & 31) ^ kswz(key)) << 4);
+      lds_dma16_s(kbase_g + kp[r >> 1] * page_bytes, off, kl + (4 * r + wg) * 1024);
+    } else {
       const int ins = 4 * r + wg;
       const int u = ins * 64 + lane;
       const int key = u / NCH;
       const int c = (u % NCH) ^ kswz(key);
       const int keyg = jj + key;
-      const int64_t pg = PAGE16 ? kp[ins >> 3] : page_id(keyg >> pshift);
+      const int64_t pg = page_id(keyg >> pshift);
       lds_dma16(kbase_g + pg * page_bytes + (int64_t)(keyg & (psize - 1)) * D * 2 + c * 16,
-                 kl + ins * 1024);
+                kl + ins * 1024);
     }
   };
-  auto v_tile_load = [&](char* vl, int jj, const int64_t* vp) __attribute__((always_inline)) {
+  auto v_load = [&](char* vl, int jj, const int64_t* vp, int r) __attribute__((always_inline)) {
     if constexpr (PAGE16) {
-      // instruction 4 r + wg: keys 8 r .. 8 r + 7 (page r / 2), dim 64 wg + lane
-      const uint32_t off = (64 * wg + lane) * 32;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        lds_dma16_s(vbase_g + vp[r >> 1] * page_bytes + 16 * (r & 1), off, vl + (4 * r + wg) * 1024);
-      return;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
+      // keys 8 r .. 8 r + 7 of the tile (page r / 2), dim 64 wg + lane
+      lds_dma16_s(vbase_g + vp[r >> 1] * page_bytes + 16 * (r & 1), (64 * wg + opaque(lane)) * 32,
+                  vl + (4 * r + wg) * 1024);
+    } else {
       const int ins = 4 * r + wg;
       const int keyg = jj + 8 * (ins >> 2);
       const int d = 64 * (ins & 3) + lane;
-      const int64_t pg = PAGE16 ? vp[ins >> 3] : page_id(keyg >> pshift);
+      const int64_t pg = page_id(keyg >> pshift);
       lds_dma16(vbase_g + pg * page_bytes + (int64_t)d * psize * 2 + (keyg & (psize - 1)) * 2,
-                 vl + ins * 1024);
+                vl + ins * 1024);
     }
   };
   auto v_tile_sanitize = [&](char* vl, int jj) __attribute__((always_inline)) {
@@ -340,7 +356,8 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   {
     int64_t p0[2] = {0, 0};
     fetch_pids(grp, p0);
-    k_tile_load(grp == 0 ? kb0 : kb1, (jt0 + grp) * KT, p0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) k_load(grp == 0 ? kb0 : kb1, (jt0 + grp) * KT, p0, r);
     // 8 instructions per half, each 4 whole half-rows (16 lanes per row);
     // rows past qo_len read the last row of the request (never stored)
 #pragma unroll
@@ -366,17 +383,20 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   auto alu_phase = [&](int j) __attribute__((always_inline)) {
     int64_t tn[2] = {0, 0};
     fetch_pids(j + 3, tn);
-    if (grp == 0) {
-      k_tile_load(kbuf(j + 2), (jt0 + j + 2) * KT, tpid);
-    } else {
-      if (j < 0) {
-        rare_path();
-        int64_t p0[2] = {0, 0};
-        fetch_pids(0, p0);
-        v_tile_load(vbuf(0), jt0 * KT, p0);
-      }
-      v_tile_load(vbuf(j + 2), (jt0 + j + 2) * KT, tpid);
+    // this group's load instruction r of K(j+2) (group 0) or V(j+2) (group 1)
+    auto issue = [&](int r) __attribute__((always_inline)) {
+      if (grp == 0) k_load(kbuf(j + 2), (jt0 + j + 2) * KT, tpid, r);
+      else v_load(vbuf(j + 2), (jt0 + j + 2) * KT, tpid, r);
+    };
+    if (grp == 1 && j < 0) {
+      rare_path();
+      int64_t p0[2] = {0, 0};
+      fetch_pids(0, p0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v_load(vbuf(0), jt0 * KT, p0, r);
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) issue(r);
     if (j >= 0 && j < ntiles) softmax((jt0 + j) * KT);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(4 | 0x70 | 0xF00);  // vmcnt(4): ALU(j-1)'s loads landed
@@ -384,22 +404,32 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
     if (grp == 1) v_tile_sanitize(vbuf(j + 1), (jt0 + j + 1) * KT);
 #pragma unroll
     for (int p = 0; p < 2; ++p) tpid[p] = tn[p];
+    // first operands of MFMA(j+1): V(j) (resident since the end of slot
+    // 2j), or K(0) before the first phase
+    if (j >= 0) preload(std::true_type{}, vbuf(j), kbuf(j + 1));
+    else preload(std::false_type{}, vbuf(0), kbuf(0));
     lds_barrier();
   };
-  // MFMA(u): PV(u-1) from V(u-1), QK(u) from K(u)
-  auto mfma_phase_t = [&](int u, int KB, int VBP) __attribute__((always_inline)) {
-    mfma_phase(vbuf(VBP), u >= 1, kbuf(KB), u < ntiles);
+  // MFMA(u): PV(u-1) from V(u-1) (if u >= 1), QK(u) from K(u) (if u <
+  // ntiles), operands preloaded
+  auto mfma_phase = [&](int u, auto pv_c, auto qk_c) __attribute__((always_inline)) {
+    mfma_seq(pv_c, qk_c, vbuf(u + 2), kbuf(u));
     lds_barrier();
   };
-  // loop body u >= 1 (compile-time u % 3 picks the buffers)
 
   fetch_pids(grp == 0 ? 2 : 1, tpid);
   // group 1 starts with ALU(-1) (no softmax, the first V loads); group 0
   // with MFMA(0)
-  for (int u = 0; u <= ntiles; ++u) {
-    if (grp == 1 || u > 0) alu_phase(u - 1);
-    mfma_phase_t(u, u, u + 2);
+  // the first MFMA phase (QK only) and the last (PV only) are peeled off
+  if (grp == 0) preload(std::false_type{}, vbuf(0), kbuf(0));
+  else alu_phase(-1);
+  mfma_phase(0, std::false_type{}, std::true_type{});
+  for (int u = 1; u < ntiles; ++u) {
+    alu_phase(u - 1);
+    mfma_phase(u, std::true_type{}, std::true_type{});
   }
+  alu_phase(ntiles - 1);
+  mfma_phase(ntiles, std::true_type{}, std::false_type{});
   // tail: group 0 matches group 1's extra lead-in barrier
   if (grp == 0) lds_barrier();
   // every wave's tile loads landed: all of LDS is free
