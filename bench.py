@@ -22,6 +22,17 @@ figures (TFLOP/s against the bf16 MFMA peak, GB/s against HBM) are under
 workload on this host.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--rows a,b] [--no-cpu]
+
+`roofline.traffic` is the measured HBM traffic of one launch of the prefill
+kernel, read from profiles/hbm_traffic.md when that summary was taken from the
+current kernel sources (their digest is recorded there), else null.  The
+summary is written by
+
+    python bench.py --pmc-summary FETCH.csv WRITE.csv --copy-mib 256
+
+from two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE) of
+`bench.py --copy-mib 256 ...`: each counter is scaled by what it reads for the
+plain device copy that --copy-mib runs first (a known number of bytes).
 """
 from __future__ import annotations
 
@@ -39,6 +50,91 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "windowed paged prefill TFLOP/s (% MFMA peak); seq_len-1 decode KV GB/s"
+HEAD_KERNEL = "prefill256_pp_kernel<true, true>"   # bf16 output, 16-slot pages
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+CALIB_KERNEL = "neg_kernel"   # the plain device copy run by --copy-mib
+
+
+def source_digest():
+    """sha256 over the kernel sources (every file of the package's csrc/)."""
+    import hashlib
+    d = os.path.join(ROOT, "paged_sliding_window_page_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as fh:
+            h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def short_kernel_name(name):
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    name = name.replace("psw_dev::", "").split("(")[0]
+    return name
+
+
+def pmc_summary(fetch_csv, write_csv, copy_mib):
+    """Markdown summary of two rocprofv3 counter runs, bytes per dispatch."""
+    import csv
+    import collections
+    import statistics
+
+    def per_kernel(path, counter):
+        per = collections.defaultdict(float)
+        name = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+                name[r["Dispatch_Id"]] = r["Kernel_Name"]
+        out = collections.defaultdict(list)
+        for d, v in per.items():
+            out[short_kernel_name(name[d])].append(v)
+        return out
+
+    fk = per_kernel(fetch_csv, "FETCH_SIZE")
+    wk = per_kernel(write_csv, "WRITE_SIZE")
+    calib = [k for k in fk if CALIB_KERNEL in k]
+    if not calib:
+        raise SystemExit(f"no {CALIB_KERNEL} dispatch in {fetch_csv}: run bench.py with --copy-mib")
+    copy_bytes = float(copy_mib) * (1 << 20)
+    f_fac = copy_bytes / (statistics.median(fk[calib[0]]) * 1024.0)
+    w_fac = copy_bytes / (statistics.median(wk[calib[0]]) * 1024.0)
+    lines = ["# HBM traffic per launch, from hardware counters", "",
+             f"source_digest: {source_digest()}",
+             f"calibration: plain copy of {copy_mib} MiB ({calib[0]}): "
+             f"bytes read = FETCH_SIZE KiB x 1024 x {f_fac:.3f}, "
+             f"bytes written = WRITE_SIZE KiB x 1024 x {w_fac:.3f}", "",
+             "| kernel | dispatches | FETCH_SIZE KiB (median) | WRITE_SIZE KiB (median) "
+             "| read MB | written MB | traffic_bytes |", "|---|---|---|---|---|---|---|"]
+    for k in sorted(fk):
+        if k not in wk or not (k.startswith("prefill") or k.startswith("attention")
+                               or k.startswith("decode") or k.startswith("merge")
+                               or k.startswith("prep")):
+            continue
+        fm = statistics.median(fk[k])
+        wm = statistics.median(wk[k])
+        rd = fm * 1024.0 * f_fac
+        wr = wm * 1024.0 * w_fac
+        lines.append(f"| `{k}` | {len(fk[k])} | {fm:.1f} | {wm:.1f} | {rd / 1e6:.2f} | "
+                     f"{wr / 1e6:.2f} | {int(round(rd + wr))} |")
+    return "\n".join(lines) + "\n"
+
+
+def read_traffic(kernel):
+    """Measured bytes per launch of `kernel`, if the summary matches the sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    digest = None
+    for line in text.splitlines():
+        if line.startswith("source_digest:"):
+            digest = line.split(":", 1)[1].strip()
+        if line.startswith(f"| `{kernel}` |") and digest == source_digest():
+            return int(line.rstrip(" |").split("|")[-1])
+    return None
 
 
 def log(*a):
@@ -245,10 +341,17 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first copy a buffer of this many MiB (device to device) three "
                          "times: the reference for scaling hardware byte counters")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the traffic summary of two rocprofv3 counter runs and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        if args.copy_mib <= 0:
+            raise SystemExit("--pmc-summary needs the --copy-mib size the runs used")
+        print(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.copy_mib), end="")
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see the sharding note in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -267,7 +370,7 @@ def main():
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)   # reads and writes copy_mib MiB
         del src, dst
     torch.cuda.synchronize()
     log("warmup ...")
@@ -319,8 +422,8 @@ def main():
         h = out_rows[head]
         res["value"] = h["achieved"]
         res["roofline"] = {"bound": "mfma", "achieved": h["achieved"], "peak": PEAK_BF16_TFLOPS,
-                           "unit": "TFLOP/s", "frac": h["frac"], "traffic": None,
-                           "kernel": "attention_kernel<256, false, true>",
+                           "unit": "TFLOP/s", "frac": h["frac"],
+                           "traffic": read_traffic(HEAD_KERNEL), "kernel": HEAD_KERNEL,
                            "algorithmic_flops_per_launch": h["work"]}
         if not args.no_cpu:
             import oracle

@@ -80,7 +80,7 @@ typedef enum {
   PSW_E_PLAN = -7,      /* plan disagrees with the pool, the entry, its compiled
                            tile, or the stream it was created on                  */
   PSW_E_HIP = -8,       /* a HIP runtime call failed (message has the HIP error)   */
-  PSW_E_UNSUPPORTED = -9 /* a geometry this build has no kernel for               */
+  PSW_E_UNSUPPORTED = -9 /* a geometry the library has no kernel for              */
 } psw_status;
 
 /* Thread-local description of the last failure on this thread ("" if none). */
