@@ -76,6 +76,11 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   constexpr int TILE = KT * D * 2; // 16 KiB
   constexpr int NW = 8;
   constexpr int AH = 3;            // LDS operand reads in flight ahead of the MFMAs
+  // O and the row sums are rescaled only when a row's maximum rises by more
+  // than kSlack (log2 units) over the one they are scaled to: P then stays
+  // below 2^20, far inside the range of bf16 and of the fp32 sums, and the
+  // rescale (128 multiplies per lane) is rare.
+  constexpr float kSlack = 20.0f;
 
   __shared__ __attribute__((aligned(1024))) char kb0[TILE];
   __shared__ __attribute__((aligned(1024))) char kb1[TILE];
@@ -263,7 +268,7 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
     }
     mx = max_with_partner_half(mx);
     const float m_new = fmaxf(m_run, mx);
-    const bool need = __any(m_new > m_run + kRescaleSlack);
+    const bool need = __any(m_new > m_run + kSlack);
     const float m_use = need ? m_new : m_run;
     const float cmul = full ? c2 : 1.0f;
     float lsum = 0.0f;
@@ -304,11 +309,9 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   // 1 KiB per tile).  kp / vp: the tile's two page ids (16-slot pages).
   auto k_load = [&](char* kl, int jj, const int64_t* kp, int r) __attribute__((always_inline)) {
     if constexpr (PAGE16) {
-      // key 8 r + 2 wg + h of the tile (page r / 2), chunk n ^ kswz(key);
-      // the lane offsets are recomputed at each use (registers are scarce)
-      const int ln = opaque(lane);
-      const int key = 8 * (r & 1) + 2 * wg + (ln >> 5);
-      const uint32_t off = key * D * 2 + (((ln & 31) ^ kswz(key)) << 4);
+      // key 8 r + 2 wg + h of the tile (page r / 2), chunk n ^ kswz(key)
+      const int key = 8 * (r & 1) + 2 * wg + h;
+      const uint32_t off = key * D * 2 + ((n ^ kswz(key)) << 4);
       lds_dma16_s(kbase_g + kp[r >> 1] * page_bytes, off, kl + (4 * r + wg) * 1024);
     } else {
       const int ins = 4 * r + wg;
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   auto v_load = [&](char* vl, int jj, const int64_t* vp, int r) __attribute__((always_inline)) {
     if constexpr (PAGE16) {
       // keys 8 r .. 8 r + 7 of the tile (page r / 2), dim 64 wg + lane
-      lds_dma16_s(vbase_g + vp[r >> 1] * page_bytes + 16 * (r & 1), (64 * wg + opaque(lane)) * 32,
+      lds_dma16_s(vbase_g + vp[r >> 1] * page_bytes + 16 * (r & 1), (64 * wg + lane) * 32,
                   vl + (4 * r + wg) * 1024);
     } else {
       const int ins = 4 * r + wg;

@@ -283,6 +283,16 @@ __global__ __launch_bounds__(256) void prep_hd512_kernel(PrepParams P) {
 
   __shared__ __attribute__((aligned(16))) __bf16 vstage[kPrepMaxTokens * (D + 8)];
 
+  // the rotation rows of this lane group's tokens, loaded once, alongside
+  // the first head's rows
+  float c[TPG][8], sn[TPG][8];
+#pragma unroll
+  for (int k = 0; k < TPG; ++k) {
+    const int tt = g + NG * k;
+    const int pos = it.pos0 + min(tt, it.ntok - 1);
+    load8f(P.cos + (int64_t)pos * HALF + 8 * li, c[k]);
+    load8f(P.sin + (int64_t)pos * HALF + 8 * li, sn[k]);
+  }
   for (int hd = 0; hd < heads; ++hd) {
     bf16x8 r1[TPG], r2[TPG];
 #pragma unroll
@@ -298,10 +308,6 @@ __global__ __launch_bounds__(256) void prep_hd512_kernel(PrepParams P) {
     for (int k = 0; k < TPG; ++k) {
       const int tt = g + NG * k;
       if (tt >= it.ntok) break;
-      const int pos = it.pos0 + tt;
-      float c[8], sn[8];
-      load8f(P.cos + (int64_t)pos * HALF + 8 * li, c);
-      load8f(P.sin + (int64_t)pos * HALF + 8 * li, sn);
       float x1[8], x2[8];
       widen8(r1[k], x1);
       widen8(r2[k], x2);
@@ -315,7 +321,7 @@ __global__ __launch_bounds__(256) void prep_hd512_kernel(PrepParams P) {
       __bf16* vs = vstage + tt * (D + 8);
       *reinterpret_cast<bf16x8*>(vs + 8 * li) = a;
       *reinterpret_cast<bf16x8*>(vs + HALF + 8 * li) = b;
-      norm_rope<true, true>(x1, x2, w1, w2, c, sn, inv);
+      norm_rope<true, true>(x1, x2, w1, w2, c[k], sn[k], inv);
       __bf16* dst = P.pool + page_off + (int64_t)hd * P.ps.head + (int64_t)(it.slot0 + tt) * D;
       store8_stream(dst + 8 * li, x1);
       store8_stream(dst + HALF + 8 * li, x2);
