@@ -22,12 +22,13 @@
 // rows read in the kperm order, dim-major V^T chunks), so P^T feeds the PV
 // MFMAs straight from the S^T accumulators.
 //
-// Loads are split between the groups so that each ALU phase issues four load
-// instructions per wave: group 0's ALU phase u loads K(u+2) into the buffer
-// K(u-1) left, group 1's loads V(u+2) into the buffer of V(u-1); each waits
-// for the loads of its own previous ALU phase (vmcnt(4)), group 1 zeroes the
-// keys past kv_len of the V tile that just landed, and the barrier that
-// follows publishes the tile, at least one phase before its first reader.
+// Loads are split between the groups, four load instructions per wave each
+// time: group 0 loads K(u+2) at the end of its MFMA phase u (while it waits
+// for group 1's softmax) into the buffer K(u-1) left, group 1 loads V(j+2)
+// in its ALU phase j into the buffer of V(j-1); each ALU phase waits for all
+// but the latest four loads of its wave (vmcnt(4)), group 1 zeroes the keys
+// past kv_len of the V tile that just landed, and the barrier that follows
+// publishes the tile, at least one phase before its first reader.
 #pragma once
 #include "psw_attention.hpp"
 
@@ -292,11 +293,12 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
     asm volatile("" ::"v"(pb[0]), "v"(pb[1]));
   };
 
-  // Tile loads, in the ALU phases: group 0's ALU(j) loads K(j+2), group 1's
-  // V(j+2) (ALU(-1) of group 1 also V(0)), four instructions per wave; each
-  // then waits for its loads of ALU(j-1), and group 1 zeroes the keys past
-  // kv_len of V(j+1).  With 16-slot pages the page ids of a tile are read
-  // through the scalar cache one ALU phase before its loads.
+  // Tile loads: group 0 loads K(u+2) at the end of its MFMA(u), group 1
+  // V(j+2) in its ALU(j) (ALU(-1) of group 1 also V(0)), four instructions
+  // per wave; each group's ALU phase waits for all but its latest four
+  // loads, and group 1 zeroes the keys past kv_len of V(j+1).  With 16-slot
+  // pages the page ids of a tile are read through the scalar cache in the ALU
+  // phase before its loads.
   int64_t tpid[2] = {0, 0};  // page ids of this wave's next tile
   auto fetch_pids = [&](int tile, int64_t* tp) __attribute__((always_inline)) {
     if constexpr (PAGE16) {
@@ -386,23 +388,20 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   auto alu_phase = [&](int j) __attribute__((always_inline)) {
     int64_t tn[2] = {0, 0};
     fetch_pids(j + 3, tn);
-    // this group's load instruction r of K(j+2) (group 0) or V(j+2) (group 1)
-    auto issue = [&](int r) __attribute__((always_inline)) {
-      if (grp == 0) k_load(kbuf(j + 2), (jt0 + j + 2) * KT, tpid, r);
-      else v_load(vbuf(j + 2), (jt0 + j + 2) * KT, tpid, r);
-    };
-    if (grp == 1 && j < 0) {
-      rare_path();
-      int64_t p0[2] = {0, 0};
-      fetch_pids(0, p0);
+    if (grp == 1) {
+      if (j < 0) {
+        rare_path();
+        int64_t p0[2] = {0, 0};
+        fetch_pids(0, p0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v_load(vbuf(0), jt0 * KT, p0, r);
+        for (int r = 0; r < 4; ++r) v_load(vbuf(0), jt0 * KT, p0, r);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v_load(vbuf(j + 2), (jt0 + j + 2) * KT, tpid, r);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) issue(r);
     if (j >= 0 && j < ntiles) softmax((jt0 + j) * KT);
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(4 | 0x70 | 0xF00);  // vmcnt(4): ALU(j-1)'s loads landed
+    __builtin_amdgcn_s_waitcnt(4 | 0x70 | 0xF00);  // vmcnt(4): the loads before the last landed
     asm volatile("" ::: "memory");
     if (grp == 1) v_tile_sanitize(vbuf(j + 1), (jt0 + j + 1) * KT);
 #pragma unroll
@@ -414,9 +413,15 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
     lds_barrier();
   };
   // MFMA(u): PV(u-1) from V(u-1) (if u >= 1), QK(u) from K(u) (if u <
-  // ntiles), operands preloaded
+  // ntiles), operands preloaded.  Group 0 then loads K(u+2) into the buffer
+  // of K(u-1), which both groups finished reading in the slot before, while
+  // it waits at the barrier for group 1's softmax.
   auto mfma_phase = [&](int u, auto pv_c, auto qk_c) __attribute__((always_inline)) {
     mfma_seq(pv_c, qk_c, vbuf(u + 2), kbuf(u));
+    if (decltype(qk_c)::value && grp == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) k_load(kbuf(u + 2), (jt0 + u + 2) * KT, tpid, r);
+    }
     lds_barrier();
   };
 
