@@ -5,6 +5,7 @@ workload (inputs resident in HBM before timing starts), all on one stream:
 
   prep_hd256           fused Q/K/V norm+RoPE+scatter, 8192 tokens, layer 3 of 8
   prep_hd512           fused K/V (V = weightless norm of raw K), 8192 tokens
+  prep_q_hd512         the global family's Q norm+RoPE, 8192 tokens x 16 heads
   prefill_window_hd256 windowed paged prefill, 8 requests ~ U[128, 2048], window 1023
   prefill_hd512        full paged prefill, 4 x 4096 tokens, 16 Q / 1 KV heads
   decode_local_hd256   one-token decode through the prefill entry, 64 requests,
@@ -235,6 +236,23 @@ def build_rows(torch, psw, synth, dev, want):
                             f"fused prep hd{d}, 8192 tokens at start 0, layer 3 of 8, "
                             f"1024-page pool, RoPE theta 1e4 over 16384 positions", hbm=True))
 
+    # ---- global-family query prep, 8192 tokens x 16 heads ----
+    if "prep_q_hd512" in want:
+        case = synth.prep_case(5, [8192], [0], head_dim=512, num_kv_heads=1, num_pages=1024,
+                               with_q_v=False, with_q=True)
+        plan = plan_of(case.qo_indptr, case.table, 16, 1, 512, 1024)
+        c, s = tables(512)
+        q_in, q_w = case.q_in.to(dev), case.q_norm_w.to(dev)
+        q_out = torch.empty_like(q_in)
+
+        def run(plan=plan, q_in=q_in, q_w=q_w, c=c, s=s, q_out=q_out):
+            psw.q_norm_rope_prefill_hd512(plan, q_in, q_w, c, s, 1e-6, q_out)
+        # Q read and written once, one cos and one sin row per token, the weight
+        work = float(2 * 8192 * 16 * 512 * 2 + 8192 * 256 * 4 * 2 + 512 * 2)
+        rows.append(Row("prep_q_hd512", run, work, "GB/s", "hbm",
+                        "query prep hd512, 8192 tokens x 16 heads at start 0, RoPE theta 1e4 "
+                        "over 16384 positions", hbm=True))
+
     # ---- windowed prefill hd256, batch 8 ----
     if "prefill_window_hd256" in want:
         lens = synth.uniform_lengths(8, 128, 2048, synth.generator(2))
@@ -358,8 +376,8 @@ def main():
     import synth
     import paged_sliding_window_page_amd as psw
 
-    all_rows = ["prep_hd256", "prep_hd512", "prefill_window_hd256", "prefill_hd512",
-                "decode_local_hd256", "decode_global_hd512"]
+    all_rows = ["prep_hd256", "prep_hd512", "prep_q_hd512", "prefill_window_hd256",
+                "prefill_hd512", "decode_local_hd256", "decode_global_hd512"]
     want = set(args.rows.split(",")) if args.rows else set(all_rows)
     dev = torch.device("cuda", 0)
     flush = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB

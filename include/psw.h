@@ -11,6 +11,8 @@
  *                                       scattered into the layer's pool pages
  *   k_v_norm_rope_paged_prefill_hd512   fused prep: K norm+RoPE, and V = the raw K
  *                                       normalised without weight (K's inv_rms)
+ *   q_norm_rope_prefill_hd512           the global family's Q norm+RoPE to a
+ *                                       contiguous buffer
  *
  * Sources (the pages this library implements):
  *   [P1] PR "feat(kernels): Rust wrapper for the hd256 windowed paged prefill",
@@ -235,6 +237,24 @@ int k_v_norm_rope_paged_prefill_hd512(psw_plan* plan, const psw_pool* pool, int6
                                       int64_t rope_positions, int64_t rope_cos_numel,
                                       int64_t rope_sin_numel, float eps,
                                       psw_stream_t stream);
+
+/* hd512 query prep, the global family's share of each layer's write side
+ * next to k_v_norm_rope_paged_prefill_hd512 (same per-row rule as the query
+ * part of the hd256 prep, [P2] Proposed Plan; [P3] Description for the
+ * global family's geometry):
+ *   q_out[t][h] = rope(rms(q_in[t][h]) * q_norm_w, p),  p = start_pos + t,
+ * contiguous, RoPE pairs (i, i + 256).  No pool is read or written.
+ *   q_in: device bf16 [total_qo][num_qo_heads][512]; q_norm_w: device bf16
+ *   [512]; rope_cos, rope_sin: device fp32 [rope_positions][256];
+ *   q_out: device bf16 [total_qo][num_qo_heads][512], caller-owned.
+ * Rejects (before launch): NULL plan or pointers, another stream, a plan not
+ * at head_dim 512, positions past rope_positions, table lengths that
+ * disagree, eps not finite and > 0. */
+int q_norm_rope_prefill_hd512(psw_plan* plan, const void* q_in, const void* q_norm_w,
+                              const float* rope_cos, const float* rope_sin,
+                              int64_t rope_positions, int64_t rope_cos_numel,
+                              int64_t rope_sin_numel, float eps, void* q_out,
+                              psw_stream_t stream);
 
 /* RoPE tables for the prep entries: cos/sin[p][i] of p * theta^(-2i/head_dim),
  * i < head_dim/2, p < positions, angles formed and evaluated in fp64 on the

@@ -32,7 +32,7 @@ from .bf16 import bf16_bits, bits_to_f64, to_f64, f64_to_bf16_bits, ulp_bf16
 from .layout import PoolGeometry, kv_blocks, gather_kv, kv_lengths
 from .attention import paged_attention, attention_rows, allowed_keys
 from .prep import (inv_rms, rms_norm_weighted, rope_rotate_half, qkv_prep_hd256,
-                   kv_prep_hd512, token_positions, expected_pool_writes,
+                   kv_prep_hd512, q_prep_hd512, token_positions, expected_pool_writes,
                    apply_pool_writes)
 
 __all__ = [
@@ -40,5 +40,5 @@ __all__ = [
     "PoolGeometry", "kv_blocks", "gather_kv", "kv_lengths",
     "paged_attention", "attention_rows", "allowed_keys",
     "inv_rms", "rms_norm_weighted", "rope_rotate_half", "qkv_prep_hd256",
-    "kv_prep_hd512", "token_positions", "expected_pool_writes", "apply_pool_writes",
+    "kv_prep_hd512", "q_prep_hd512", "token_positions", "expected_pool_writes", "apply_pool_writes",
 ]

@@ -9,7 +9,9 @@ hd256 QKV in one pass, hd512 V alongside K", Description and Proposed Plan):
   into the layer's pool pages.
 * hd512 (global layers): K is normalised with its weight and rotated; V is
   the raw K normalised without a weight, reusing K's normalising denominator,
-  and is not rotated.
+  and is not rotated.  The global family's Q takes the query rule of the hd256
+  prep at head_dim 512 (the pages give that rule once, for Q, without tying it
+  to a head_dim; reading taken here).
 * Slot contract: token t of a request lands at position start_pos + t, page
   ids[(start_pos + t) // P], slot (start_pos + t) % P, in the given layer.
 
@@ -89,6 +91,15 @@ def kv_prep_hd512(k_in, k_norm_w, pos, eps: float, theta: float):
     k_rows = rope_rotate_half(k * inv * wk, pos, theta)
     v_rows = k * inv
     return k_rows, v_rows
+
+
+def q_prep_hd512(q_in, q_norm_w, pos, eps: float, theta: float):
+    """Global-family query rows [T, Hq, 512]: the query rule of the hd256 prep
+    (weighted RMSNorm, then rotate-half RoPE at the token's position) at
+    head_dim 512, written contiguously."""
+    q = to_f64(q_in)
+    wq = to_f64(q_norm_w)
+    return rope_rotate_half(rms_norm_weighted(q, wq, eps), pos, theta)
 
 
 def expected_pool_writes(geom: PoolGeometry, layer: int, qo_indptr, kv_page_indptr,

@@ -9,6 +9,7 @@ built (``python -m paged_sliding_window_page_amd.build``).
 
 Names follow the C ABI: ``paged_prefill_window_hd256``, ``paged_prefill_hd512``,
 ``qkv_norm_rope_paged_prefill_hd256``, ``k_v_norm_rope_paged_prefill_hd512``,
+``q_norm_rope_prefill_hd512``,
 ``rope_tables`` (``psw_rope_tables``), and the ``Plan`` object wrapping
 ``psw_plan_*``.  Tensors are torch tensors on the current HIP device; the stream
 is torch's current stream unless one is passed.
@@ -102,6 +103,8 @@ _prep256 = _sig("qkv_norm_rope_paged_prefill_hd256", ctypes.c_int, c_vp, ctypes.
                 ctypes.c_float, c_vp, c_vp)
 _prep512 = _sig("k_v_norm_rope_paged_prefill_hd512", ctypes.c_int, c_vp, ctypes.POINTER(PoolDesc),
                 c_i64, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, ctypes.c_float, c_vp)
+_prepq512 = _sig("q_norm_rope_prefill_hd512", ctypes.c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
+                 c_i64, c_i64, ctypes.c_float, c_vp, c_vp)
 _rope = _sig("psw_rope_tables", ctypes.c_int, c_vp, c_vp, c_i64, c_i64, ctypes.c_double, c_vp)
 _dev_err = _sig("psw_plan_device_errors", ctypes.c_int, c_vp)
 
@@ -110,7 +113,7 @@ EXPORTS = ["psw_last_error", "psw_version", "psw_check_pool", "psw_plan_create",
            "psw_plan_update", "psw_plan_destroy", "psw_plan_get_info", "psw_prefill_tile_q",
            "paged_prefill_window_hd256", "paged_prefill_hd512",
            "qkv_norm_rope_paged_prefill_hd256", "k_v_norm_rope_paged_prefill_hd512",
-           "psw_rope_tables", "psw_plan_device_errors"]
+           "q_norm_rope_prefill_hd512", "psw_rope_tables", "psw_plan_device_errors"]
 
 
 def _check(rc: int):
@@ -265,6 +268,16 @@ def k_v_norm_rope_paged_prefill_hd512(plan: Plan, pool: PoolDesc, layer: int, k_
                     _ptr(rope_cos), _ptr(rope_sin), int(rope_positions), int(rope_cos.numel()),
                     int(rope_sin.numel()), float(eps),
                     plan.stream if stream is None else _stream_handle(stream)))
+
+
+def q_norm_rope_prefill_hd512(plan: Plan, q_in, q_norm_w, rope_cos, rope_sin, eps: float, q_out,
+                              rope_positions=None, stream=None) -> None:
+    if rope_positions is None:
+        rope_positions = rope_cos.shape[0]
+    _check(_prepq512(plan.handle, _ptr(q_in), _ptr(q_norm_w), _ptr(rope_cos), _ptr(rope_sin),
+                     int(rope_positions), int(rope_cos.numel()), int(rope_sin.numel()),
+                     float(eps), _ptr(q_out),
+                     plan.stream if stream is None else _stream_handle(stream)))
 
 
 def rope_tables(cos_out, sin_out, positions: int, head_dim: int, theta: float,

@@ -96,6 +96,7 @@ hipError_t launch_merge_d256(bool out_bf16, const MergeParams& p, int batch, hip
 hipError_t launch_merge_d512(bool out_bf16, const MergeParams& p, int batch, hipStream_t s);
 hipError_t launch_prep_hd256(const PrepParams& p, int n_items, hipStream_t s);
 hipError_t launch_prep_hd512(const PrepParams& p, int n_items, hipStream_t s);
+hipError_t launch_prep_q_hd512(const PrepParams& p, int n_items, hipStream_t s);
 hipError_t launch_rope_tables(float* c, float* s, int64_t positions, int64_t half, double theta,
                               hipStream_t st);
 

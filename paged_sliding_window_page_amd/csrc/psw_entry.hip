@@ -354,6 +354,45 @@ int k_v_norm_rope_paged_prefill_hd512(psw_plan* plan, const psw_pool* pool, int6
   return PSW_OK;
 }
 
+int q_norm_rope_prefill_hd512(psw_plan* plan, const void* q_in, const void* q_norm_w,
+                              const float* rope_cos, const float* rope_sin, int64_t rope_positions,
+                              int64_t rope_cos_numel, int64_t rope_sin_numel, float eps,
+                              void* q_out, psw_stream_t stream) {
+  psw::clear_error();
+  int rc = psw::check_q_prep_call(plan, 512, q_in, q_norm_w, rope_cos, rope_sin, rope_positions,
+                                  rope_cos_numel, rope_sin_numel, eps, q_out, stream);
+  if (rc) return rc;
+  if (!plan->prep_built) {
+    psw::build_prep_items(plan->st, &plan->prep_items);
+    plan->prep_built = true;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(plan->stream);
+  rc = ensure_mirror(plan);
+  if (rc) return rc;
+  psw_device_mirror* m = plan->mirror;
+  if (m->prep_gen != plan->generation) {
+    rc = upload(m, &m->prep, &m->prep_cap, m->st_prep, plan->prep_items, s);
+    if (rc) return rc;
+    m->prep_gen = plan->generation;
+  }
+  psw_dev::PrepParams p{};
+  p.cos = rope_cos;
+  p.sin = rope_sin;
+  p.err = m->err;
+  p.items = m->prep;
+  p.num_qo_heads = plan->st.num_qo_heads;
+  p.num_kv_heads = plan->st.num_kv_heads;
+  p.rope_positions = static_cast<int32_t>(rope_positions);
+  p.eps = eps;
+  p.q_in = static_cast<const __bf16*>(q_in);
+  p.q_w = static_cast<const __bf16*>(q_norm_w);
+  p.q_out = static_cast<__bf16*>(q_out);
+  const int n = static_cast<int>(plan->prep_items.size() / psw_dev::kPrepItemInts);
+  hipError_t e = psw_dev::launch_prep_q_hd512(p, n, s);
+  if (e != hipSuccess) return hip_fail(e, "prep launch");
+  return PSW_OK;
+}
+
 int psw_rope_tables(float* cos_out, float* sin_out, int64_t positions, int64_t head_dim,
                     double theta, psw_stream_t stream) {
   psw::clear_error();

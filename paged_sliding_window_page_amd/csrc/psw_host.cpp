@@ -358,13 +358,10 @@ int check_attention_call(const psw_plan* plan, const psw_pool* pool, int64_t lay
   return PSW_OK;
 }
 
-int check_prep_call(const psw_plan* plan, const psw_pool* pool, int64_t layer,
-                    int64_t want_head_dim, const float* rope_cos, const float* rope_sin,
-                    int64_t rope_positions, int64_t rope_cos_numel, int64_t rope_sin_numel,
-                    float eps, psw_stream_t stream) {
-  int rc = check_plan_vs_pool(plan, pool, layer, stream, want_head_dim);
-  if (rc != PSW_OK) return rc;
-  const PlanState& s = plan->st;
+// RoPE tables, eps and the positions the plan writes (shared by the preps).
+static int check_rope_eps(const PlanState& s, int64_t want_head_dim, const float* rope_cos,
+                          const float* rope_sin, int64_t rope_positions, int64_t rope_cos_numel,
+                          int64_t rope_sin_numel, float eps) {
   if (!rope_cos || !rope_sin) return fail(PSW_E_NULL, "RoPE table pointer is NULL");
   if (rope_positions < 1) return fail(PSW_E_SHAPE, "rope_positions must be >= 1");
   if (!fits_i32(rope_positions)) return fail(PSW_E_OVERFLOW, "rope_positions past INT32_MAX");
@@ -380,6 +377,19 @@ int check_prep_call(const psw_plan* plan, const psw_pool* pool, int64_t layer,
     return fail(PSW_E_RANGE, "position " + std::to_string(s.max_kv_len - 1) +
                                  " is past the RoPE table of " + std::to_string(rope_positions) +
                                  " positions");
+  return PSW_OK;
+}
+
+int check_prep_call(const psw_plan* plan, const psw_pool* pool, int64_t layer,
+                    int64_t want_head_dim, const float* rope_cos, const float* rope_sin,
+                    int64_t rope_positions, int64_t rope_cos_numel, int64_t rope_sin_numel,
+                    float eps, psw_stream_t stream) {
+  int rc = check_plan_vs_pool(plan, pool, layer, stream, want_head_dim);
+  if (rc != PSW_OK) return rc;
+  const PlanState& s = plan->st;
+  rc = check_rope_eps(s, want_head_dim, rope_cos, rope_sin, rope_positions, rope_cos_numel,
+                      rope_sin_numel, eps);
+  if (rc != PSW_OK) return rc;
   // every written position has a page, and no page is written twice
   std::unordered_set<int32_t> written;
   for (int32_t b = 0; b < s.batch; ++b) {
@@ -397,6 +407,22 @@ int check_prep_call(const psw_plan* plan, const psw_pool* pool, int64_t layer,
     }
   }
   return PSW_OK;
+}
+
+int check_q_prep_call(const psw_plan* plan, int64_t want_head_dim, const void* q_in,
+                      const void* q_norm_w, const float* rope_cos, const float* rope_sin,
+                      int64_t rope_positions, int64_t rope_cos_numel, int64_t rope_sin_numel,
+                      float eps, const void* q_out, psw_stream_t stream) {
+  if (!plan) return fail(PSW_E_NULL, "plan is NULL");
+  const PlanState& s = plan->st;
+  if (stream != plan->stream)
+    return fail(PSW_E_PLAN, "stream differs from the stream the plan was created on");
+  if (s.head_dim != want_head_dim)
+    return fail(PSW_E_PLAN, "entry is for head_dim " + std::to_string(want_head_dim) +
+                                ", plan has " + std::to_string(s.head_dim));
+  if (!q_in || !q_norm_w || !q_out) return fail(PSW_E_NULL, "q_in, q_norm_w or q_out is NULL");
+  return check_rope_eps(s, want_head_dim, rope_cos, rope_sin, rope_positions, rope_cos_numel,
+                        rope_sin_numel, eps);
 }
 
 }  // namespace psw

@@ -110,6 +110,12 @@ int check_prep_call(const psw_plan* plan, const psw_pool* pool, int64_t layer,
                     int64_t rope_positions, int64_t rope_cos_numel, int64_t rope_sin_numel,
                     float eps, psw_stream_t stream);
 
+// Checks of the query-only prep entry (no pool) before any HIP call.
+int check_q_prep_call(const psw_plan* plan, int64_t want_head_dim, const void* q_in,
+                      const void* q_norm_w, const float* rope_cos, const float* rope_sin,
+                      int64_t rope_positions, int64_t rope_cos_numel, int64_t rope_sin_numel,
+                      float eps, const void* q_out, psw_stream_t stream);
+
 }  // namespace psw
 
 // Device mirror (defined in the HIP translation unit; opaque here).

@@ -332,6 +332,70 @@ __global__ __launch_bounds__(256) void prep_hd512_kernel(PrepParams P) {
   }
 }
 
+// hd512 query prep: q_out row = rope(rms(q_in row) * q_norm_w, p), written
+// contiguously.  Work-group: one item (<= 16 consecutive positions of one
+// request) x kQHeads heads; lane group g (32 lanes) owns tokens g and g + 8 of
+// the item, all of the work-group's heads, so a token's rotation rows are read
+// once.  Only positions are checked on the device (no pool is touched).
+constexpr int kQHeads = 4;
+__global__ __launch_bounds__(256) void prep_q_hd512_kernel(PrepParams P) {
+  constexpr int D = 512, LPR = 32, HALF = D / 2, NG = 256 / LPR, HG = kQHeads;
+  constexpr int TPG = kPrepMaxTokens / NG;  // tokens per lane group
+  const Item it = read_item(P.items + kPrepItemInts * blockIdx.x);
+  const bool ok = it.pos0 >= 0 && it.ntok >= 1 && it.ntok <= kPrepMaxTokens &&
+                  it.pos0 + it.ntok <= P.rope_positions;
+  if (!ok) {
+    if (threadIdx.x == 0) {
+      P.err[0] = 1;
+      P.err[1] = -1;
+      P.err[2] = it.pos0 + it.ntok - 1;
+    }
+    return;
+  }
+  const int li = threadIdx.x % LPR;
+  const int g = threadIdx.x / LPR;
+  const int h0 = HG * blockIdx.y;
+  const int hcount = min(HG, P.num_qo_heads - h0);
+  float w1[8], w2[8];
+  load8(P.q_w + 8 * li, w1);
+  load8(P.q_w + HALF + 8 * li, w2);
+  // every load of the lane group first: rows and rotation rows in flight together
+  float c[TPG][8], sn[TPG][8];
+  bf16x8 r1[TPG][HG], r2[TPG][HG];
+#pragma unroll
+  for (int k = 0; k < TPG; ++k) {
+    const int tt = g + NG * k;
+    if (tt >= it.ntok) break;
+    const int pos = it.pos0 + tt;
+    load8f(P.cos + (int64_t)pos * HALF + 8 * li, c[k]);
+    load8f(P.sin + (int64_t)pos * HALF + 8 * li, sn[k]);
+    const __bf16* src = P.q_in + ((int64_t)(it.tok0 + tt) * P.num_qo_heads + h0) * D;
+#pragma unroll
+    for (int h = 0; h < HG; ++h)
+      if (h < hcount) {
+        r1[k][h] = load8_stream(src + h * D + 8 * li);
+        r2[k][h] = load8_stream(src + h * D + HALF + 8 * li);
+      }
+  }
+#pragma unroll
+  for (int k = 0; k < TPG; ++k) {
+    const int tt = g + NG * k;
+    if (tt >= it.ntok) break;
+#pragma unroll
+    for (int h = 0; h < HG; ++h) {
+      if (h >= hcount) break;
+      float x1[8], x2[8];
+      widen8(r1[k][h], x1);
+      widen8(r2[k][h], x2);
+      const float inv = inv_rms<LPR>(x1, x2, 1.0f / D, P.eps);
+      norm_rope<true, true>(x1, x2, w1, w2, c[k], sn[k], inv);
+      __bf16* dst = P.q_out + ((int64_t)(it.tok0 + tt) * P.num_qo_heads + h0 + h) * D;
+      store8_stream(dst + 8 * li, x1);
+      store8_stream(dst + HALF + 8 * li, x2);
+    }
+  }
+}
+
 // cos/sin[p][i] = cos/sin(p * theta^(-2i/D)), formed and evaluated in fp64.
 __global__ void rope_table_kernel(float* __restrict__ c, float* __restrict__ s, int64_t positions,
                                   int64_t half, double theta) {
@@ -357,6 +421,13 @@ hipError_t launch_prep_hd256(const PrepParams& p, int n_items, hipStream_t s) {
 hipError_t launch_prep_hd512(const PrepParams& p, int n_items, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
   hipLaunchKernelGGL(prep_hd512_kernel, dim3(n_items), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_q_hd512(const PrepParams& p, int n_items, hipStream_t s) {
+  if (n_items <= 0) return hipSuccess;
+  const int groups = (p.num_qo_heads + kQHeads - 1) / kQHeads;
+  hipLaunchKernelGGL(prep_q_hd512_kernel, dim3(n_items, groups), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -195,7 +195,7 @@ def prep_case(seed: int, qo_lens, start_pos, *, head_dim: int, num_kv_heads: int
               num_qo_heads: int = 16, page_size: int = 16, num_pages: int | None = None,
               num_layers: int = 8, layer: int = 3, rope_positions: int = 16384,
               rope_theta: float = 10000.0, eps: float = 1e-6, with_q_v: bool = True,
-              extra_pages: int = 0) -> PrepCase:
+              extra_pages: int = 0, with_q: bool = False) -> PrepCase:
     """Projections ~ N(0, 1) in bf16, norm weights 1 + N(0, 0.1^2) in bf16.
 
     Request b writes tokens at positions start_pos[b] .. start_pos[b]+qo_lens[b]-1,
@@ -212,6 +212,11 @@ def prep_case(seed: int, qo_lens, start_pos, *, head_dim: int, num_kv_heads: int
     v_in = normal_bf16((t, num_kv_heads, head_dim), 1.0, gen) if with_q_v else None
     q_w = normal_bf16((head_dim,), 0.1, gen, mean=1.0) if with_q_v else None
     k_w = normal_bf16((head_dim,), 0.1, gen, mean=1.0)
+    if with_q and not with_q_v:
+        # queries without V (the global family), drawn after everything else so
+        # the K-only cases keep their inputs
+        q_in = normal_bf16((t, num_qo_heads, head_dim), 1.0, gen)
+        q_w = normal_bf16((head_dim,), 0.1, gen, mean=1.0)
     return PrepCase(head_dim, num_qo_heads, num_kv_heads, page_size, num_pages, num_layers,
                     layer, list(map(int, qo_lens)), kv_lens, lengths_to_indptr(qo_lens), table,
                     q_in, k_in, v_in, q_w, k_w, rope_positions, rope_theta, eps)

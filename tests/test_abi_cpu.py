@@ -284,6 +284,39 @@ def test_prep512_rejects_hd256_plan():
     assert code == "PSW_E_PLAN"
 
 
+def _prepq(plan, positions=32, cos_numel=None, sin_numel=None, eps=1e-6, stream=0, q_in=FAKE,
+           w=FAKE, cos=FAKE, q_out=FAKE):
+    cn = positions * 256 if cos_numel is None else cos_numel
+    sn = positions * 256 if sin_numel is None else sin_numel
+    return psw._check(psw._prepq512(None if plan is None else plan.handle, q_in, w, cos, FAKE,
+                                    positions, cn, sn, eps, q_out, stream))
+
+
+def _plan512(**over):
+    return _plan(**_plan_args(num_kv_heads=1, head_dim=512, **over))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(positions=19), "PSW_E_RANGE"),          # kv_len 20 -> last position 19
+    (dict(cos_numel=32 * 256 - 1), "PSW_E_SHAPE"),
+    (dict(sin_numel=32 * 128), "PSW_E_SHAPE"),
+    (dict(eps=0.0), "PSW_E_SCALE"),
+    (dict(eps=math.inf), "PSW_E_SCALE"),
+    (dict(stream=5), "PSW_E_PLAN"),
+    (dict(q_in=None), "PSW_E_NULL"),
+    (dict(w=None), "PSW_E_NULL"),
+    (dict(cos=None), "PSW_E_NULL"),
+    (dict(q_out=None), "PSW_E_NULL"),
+])
+def test_query_prep512_rejects(kw, status):
+    assert _code(lambda: _prepq(_plan512(), **kw)) == status
+
+
+def test_query_prep512_rejects_null_plan_and_hd256_plan():
+    assert _code(lambda: _prepq(None)) == "PSW_E_NULL"
+    assert _code(lambda: _prepq(_plan())) == "PSW_E_PLAN"
+
+
 def test_rope_table_rejects():
     assert _code(lambda: psw.rope_tables(FAKE, FAKE, 0, 256, 1e4, stream=0)) == "PSW_E_SHAPE"
     assert _code(lambda: psw.rope_tables(FAKE, FAKE, 16, 255, 1e4, stream=0)) == "PSW_E_SHAPE"

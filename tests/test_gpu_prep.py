@@ -165,6 +165,84 @@ def test_prep_8192_tokens_layer3_of_8(d):
     _check_prep(case, d, g, pool, q_out, sample_tokens=toks)
 
 
+def _run_query_prep(case, label):
+    say(f"[gpu] query prep hd512 {label} tokens={sum(case.qo_lens)}")
+    c, s = _tables(case.rope_positions, 512, case.rope_theta)
+    plan = psw.Plan(case.qo_indptr, case.table.kv_page_indptr, case.table.kv_page_indices,
+                    case.table.kv_last_page_len, num_qo_heads=case.num_qo_heads,
+                    num_kv_heads=case.num_kv_heads, head_dim=512, page_size=case.page_size,
+                    num_pages=case.num_pages)
+    q_out = torch.full(case.q_in.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    psw.q_norm_rope_prefill_hd512(plan, case.q_in.to(DEV), case.q_norm_w.to(DEV), c, s,
+                                  case.eps, q_out)
+    torch.cuda.synchronize()
+    plan.device_errors()
+    plan.close()
+    return q_out
+
+
+@pytest.mark.parametrize("qo,start", [([40], [0]), ([5, 33, 16, 1], [11, 0, 48, 300]),
+                                      ([1], [0]), ([17], [15])])
+def test_hd512_query_prep_values(qo, start):
+    """Global-family Q prep: every row written (no NaN left of the fill), values
+    against the oracle at the token's position."""
+    case = synth.prep_case(90 + len(qo), qo, start, head_dim=512, num_kv_heads=1,
+                           with_q_v=False, with_q=True, rope_positions=512)
+    q_out = _run_query_prep(case, f"{qo}@{start}")
+    assert not bool(torch.isnan(q_out).any()), "a query row was not written"
+    pos = oracle.token_positions(case.qo_indptr, case.table.kv_page_indptr,
+                                 case.table.kv_last_page_len, case.page_size)
+    ref = oracle.q_prep_hd512(case.q_in, case.q_norm_w, pos, case.eps, case.rope_theta)
+    check_close(to_np64(q_out), ref, "q_out hd512")
+    exact = np.mean(oracle.f64_to_bf16_bits(ref) == oracle.bf16_bits(q_out.cpu()))
+    say(f"  q_out bitwise equal to RNE(oracle): {exact:.6f}")
+
+
+def test_hd512_query_prep_8192_tokens():
+    """8192 tokens x 16 heads at start 0, tables for 16384 positions: every row
+    written, values on sampled tokens."""
+    case = synth.prep_case(5, [8192], [0], head_dim=512, num_kv_heads=1, num_pages=1024,
+                           with_q_v=False, with_q=True, rope_positions=16384)
+    q_out = _run_query_prep(case, "8192")
+    assert not bool(torch.isnan(q_out).any()), "a query row was not written"
+    rng = np.random.default_rng(5)
+    toks = np.unique(np.concatenate([rng.integers(0, 8192, 90), [0, 1, 15, 16, 8190, 8191]]))
+    ref = oracle.q_prep_hd512(case.q_in[toks], case.q_norm_w, toks, case.eps, case.rope_theta)
+    check_close(to_np64(q_out[torch.from_numpy(toks).to(DEV)]), ref, "q_out hd512 sampled")
+
+
+def test_global_layer_write_side_then_attention():
+    """One global layer end to end from the raw projections: Q prep and K/V prep
+    write the query buffer and the pool, then full attention reads both; the
+    oracle chain rounds every stored row to bf16 like the GPU stores do."""
+    # every key is written by this prep (start 0), so attention reads no unwritten slot
+    case = synth.prep_case(83, [70, 190], [0, 0], head_dim=512, num_kv_heads=1, num_layers=2,
+                           layer=1, with_q_v=False, with_q=True, rope_positions=1024,
+                           extra_pages=3)
+    g, pool, _ = _run_prep(case, 512, "layer chain")
+    q_dev = _run_query_prep(case, "layer chain")
+    t = case.table
+    acase = synth.AttentionCase(16, 1, 512, 16, case.num_pages, 2, 1, case.qo_lens, case.kv_lens,
+                                case.qo_indptr, t, q_dev.cpu(), pool)
+    from gpu_util import run_attention
+    gpu = run_attention(acase, pool=pool, label="layer chain attention")
+    pos = oracle.token_positions(case.qo_indptr, t.kv_page_indptr, t.kv_last_page_len,
+                                 case.page_size)
+    q_ref = oracle.bits_to_f64(oracle.f64_to_bf16_bits(
+        oracle.q_prep_hd512(case.q_in, case.q_norm_w, pos, case.eps, case.rope_theta)))
+    k_ref, v_ref = oracle.kv_prep_hd512(case.k_in, case.k_norm_w, pos, case.eps, case.rope_theta)
+    store = np.zeros(g.numel, dtype=np.float64)
+    page, slot = oracle.expected_pool_writes(g, 1, case.qo_indptr, t.kv_page_indptr,
+                                             t.kv_page_indices, t.kv_last_page_len)
+    oracle.apply_pool_writes(store, g, 1, page, slot,
+                             oracle.bits_to_f64(oracle.f64_to_bf16_bits(k_ref)),
+                             oracle.bits_to_f64(oracle.f64_to_bf16_bits(v_ref)))
+    ref = oracle.paged_attention(oracle.f64_to_bf16_bits(q_ref), oracle.f64_to_bf16_bits(store),
+                                 g, 1, case.qo_indptr, t.kv_page_indptr, t.kv_page_indices,
+                                 t.kv_last_page_len, 1.0, -1)
+    check_close(gpu, ref, "Q prep + K/V prep -> attention")
+
+
 def test_prep_then_attention_hd512_chain():
     """The global family's write side feeding its read side: prep writes K and V
     for 300 tokens, then full attention reads them back through the same pages."""

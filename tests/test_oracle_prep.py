@@ -138,6 +138,26 @@ def test_hd512_v_is_weightless_norm_of_raw_k():
     np.testing.assert_allclose(k_rows, _hf_rope(v_rows * wk, pos, 1e4), atol=1e-4)
 
 
+def test_hd512_query_prep():
+    """Global-family Q: torch's weighted rms_norm at position 0 (rotation is the
+    identity there), the transformers rotate-half rotation at head_dim 512
+    elsewhere, and pair norms = those of the normalised rows."""
+    case = synth.prep_case(11, [20], [300], head_dim=512, num_kv_heads=1, with_q_v=False,
+                           with_q=True)
+    pos = 300 + np.arange(20)
+    q_out = oracle.q_prep_hd512(case.q_in, case.q_norm_w, pos, case.eps, case.rope_theta)
+    assert q_out.shape == (20, 16, 512)
+    q = torch.from_numpy(oracle.to_f64(case.q_in))
+    wq = torch.from_numpy(oracle.to_f64(case.q_norm_w))
+    qn = torch.nn.functional.rms_norm(q, (512,), wq, 1e-6).numpy()
+    at0 = oracle.q_prep_hd512(case.q_in[:1], case.q_norm_w, np.array([0]), case.eps,
+                              case.rope_theta)
+    np.testing.assert_allclose(at0, qn[:1], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(q_out, _hf_rope(qn, pos, 1e4), atol=2e-3)
+    np.testing.assert_allclose(q_out[..., :256] ** 2 + q_out[..., 256:] ** 2,
+                               qn[..., :256] ** 2 + qn[..., 256:] ** 2, rtol=1e-11)
+
+
 def test_hd512_unit_weight_position_zero_gives_k_equal_v():
     k = synth.normal_bf16((1, 1, 512), 1.0, synth.generator(3))
     w = torch.ones(512, dtype=torch.bfloat16)
