@@ -262,6 +262,79 @@ int q_norm_rope_prefill_hd512(psw_plan* plan, const void* q_in, const void* q_no
 int psw_rope_tables(float* cos_out, float* sin_out, int64_t positions, int64_t head_dim,
                     double theta, psw_stream_t stream);
 
+/* --------------------------------------------- two-family page accounting ---- */
+
+/* Host-side page accounting for serving from two KV families at once ([P3]
+ * Description: a pool per family, a per-request state in each, admission that
+ * keeps the two pools consistent; [P3] review thread: the KV frontier moves
+ * only after a successful step).  No device memory is involved: the server
+ * hands out page ids of the two caller-owned pools (psw_pool), and
+ * psw_kv_step_tables turns a batch of admitted steps into the CSR metadata of
+ * psw_plan_desc.  Not thread-safe: one host thread drives a server.
+ *
+ * A request has one frontier F (its KV length, the same in both families) and
+ * holds exactly ceil(F / page_size_f) pages of family f.  A step of n tokens:
+ *   psw_kv_admit   checks, before any state changes: the request belongs to
+ *                  this server, no step is pending, the held pages match F,
+ *                  F + n <= rope_positions, and F + n <= window_left + 1 when
+ *                  window_left >= 0 (slots equal absolute positions only
+ *                  until the window starts dropping keys; this path refuses
+ *                  to cross it).  Then it reserves ceil((F+n)/P_f) - held_f
+ *                  pages of both families; if either pool is short, nothing
+ *                  is kept: both pools end exactly as they were (the same free
+ *                  ids in the same order) and PSW_E_RANGE is returned.
+ *   psw_kv_commit  after the step succeeded: the reserved pages join the held
+ *                  ones and F += n.
+ *   psw_kv_abort   after a failed step: the reserved pages go back, F stays.
+ * Page ids are handed out lowest first from a fresh pool, and a pool's free
+ * list is last-in first-out. */
+enum { PSW_KV_LOCAL = 0, PSW_KV_GLOBAL = 1 };
+
+typedef struct {
+  int64_t local_pages, global_pages;            /* pool sizes (page ids 0..n-1)   */
+  int64_t local_page_size, global_page_size;    /* slots per page                 */
+  int64_t window_left;                          /* local window (inclusive), -1 */
+  int64_t rope_positions;                       /* positions the RoPE tables hold */
+} psw_kv_server_desc;
+
+typedef struct psw_kv_server psw_kv_server;     /* opaque: the two pools         */
+typedef struct psw_kv_request psw_kv_request;   /* opaque: one request's state   */
+
+typedef struct {
+  int64_t frontier;                             /* committed KV length            */
+  int64_t local_held, global_held;              /* committed pages per family     */
+  int32_t pending;                              /* 1 while a step is admitted     */
+  int64_t pending_tokens;                       /* its token count                */
+  int64_t local_reserved, global_reserved;      /* its reserved pages             */
+} psw_kv_request_state;
+
+/* Rejects: NULL pointers, pools or page sizes < 1, window_left < -1,
+ * rope_positions < 1, extents past INT32_MAX. */
+int psw_kv_server_create(const psw_kv_server_desc* desc, psw_kv_server** out);
+/* PSW_E_PLAN while requests of this server are not released (nothing freed). */
+int psw_kv_server_destroy(psw_kv_server* server);
+int psw_kv_server_free_pages(const psw_kv_server* server, int64_t* local_free,
+                             int64_t* global_free);
+/* A request with F = 0 and no pages. */
+int psw_kv_request_create(psw_kv_server* server, psw_kv_request** out);
+/* Returns every held and reserved page to the pools and frees the state;
+ * PSW_E_PLAN for a request of another server. */
+int psw_kv_request_release(psw_kv_server* server, psw_kv_request* request);
+int psw_kv_request_info(const psw_kv_request* request, psw_kv_request_state* out);
+int psw_kv_admit(psw_kv_server* server, psw_kv_request* request, int64_t n_new);
+int psw_kv_commit(psw_kv_server* server, psw_kv_request* request);
+int psw_kv_abort(psw_kv_server* server, psw_kv_request* request);
+/* CSR tables of one family for a batch of requests that each have a step
+ * pending: request b's queries are its n_b new tokens, its pages the held then
+ * the reserved ones, its KV length F_b + n_b.  Host arrays: qo_indptr and
+ * kv_page_indptr [n_reqs + 1], kv_last_page_len [n_reqs], kv_page_indices of
+ * indices_cap entries (PSW_E_SHAPE when too small).  Also rejects a request
+ * listed twice, one without a pending step, and one of another server. */
+int psw_kv_step_tables(const psw_kv_server* server, psw_kv_request* const* requests,
+                       int64_t n_reqs, int32_t family, int32_t* qo_indptr,
+                       int32_t* kv_page_indptr, int32_t* kv_page_indices,
+                       int64_t indices_cap, int32_t* kv_last_page_len);
+
 /* ----------------------------------------------------------- device check ---- */
 
 /* Second line of defence inside the prep kernels ([P2] Proposed Plan): a

@@ -78,6 +78,17 @@ class PlanInfo(ctypes.Structure):
                 ("digest", ctypes.c_uint64)]
 
 
+class KvServerDesc(ctypes.Structure):
+    _fields_ = [("local_pages", c_i64), ("global_pages", c_i64), ("local_page_size", c_i64),
+                ("global_page_size", c_i64), ("window_left", c_i64), ("rope_positions", c_i64)]
+
+
+class KvRequestState(ctypes.Structure):
+    _fields_ = [("frontier", c_i64), ("local_held", c_i64), ("global_held", c_i64),
+                ("pending", c_i32), ("pending_tokens", c_i64), ("local_reserved", c_i64),
+                ("global_reserved", c_i64)]
+
+
 def _sig(name, res, *args):
     f = getattr(_lib, name)
     f.restype = res
@@ -105,6 +116,19 @@ _prep512 = _sig("k_v_norm_rope_paged_prefill_hd512", ctypes.c_int, c_vp, ctypes.
                 c_i64, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, ctypes.c_float, c_vp)
 _prepq512 = _sig("q_norm_rope_prefill_hd512", ctypes.c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
                  c_i64, c_i64, ctypes.c_float, c_vp, c_vp)
+_kv_create = _sig("psw_kv_server_create", ctypes.c_int, ctypes.POINTER(KvServerDesc),
+                  ctypes.POINTER(c_vp))
+_kv_destroy = _sig("psw_kv_server_destroy", ctypes.c_int, c_vp)
+_kv_free = _sig("psw_kv_server_free_pages", ctypes.c_int, c_vp, ctypes.POINTER(c_i64),
+                ctypes.POINTER(c_i64))
+_kv_req_create = _sig("psw_kv_request_create", ctypes.c_int, c_vp, ctypes.POINTER(c_vp))
+_kv_req_release = _sig("psw_kv_request_release", ctypes.c_int, c_vp, c_vp)
+_kv_req_info = _sig("psw_kv_request_info", ctypes.c_int, c_vp, ctypes.POINTER(KvRequestState))
+_kv_admit = _sig("psw_kv_admit", ctypes.c_int, c_vp, c_vp, c_i64)
+_kv_commit = _sig("psw_kv_commit", ctypes.c_int, c_vp, c_vp)
+_kv_abort = _sig("psw_kv_abort", ctypes.c_int, c_vp, c_vp)
+_kv_tables = _sig("psw_kv_step_tables", ctypes.c_int, c_vp, ctypes.POINTER(c_vp), c_i64, c_i32,
+                  c_i32p, c_i32p, c_i32p, c_i64, c_i32p)
 _rope = _sig("psw_rope_tables", ctypes.c_int, c_vp, c_vp, c_i64, c_i64, ctypes.c_double, c_vp)
 _dev_err = _sig("psw_plan_device_errors", ctypes.c_int, c_vp)
 
@@ -113,7 +137,10 @@ EXPORTS = ["psw_last_error", "psw_version", "psw_check_pool", "psw_plan_create",
            "psw_plan_update", "psw_plan_destroy", "psw_plan_get_info", "psw_prefill_tile_q",
            "paged_prefill_window_hd256", "paged_prefill_hd512",
            "qkv_norm_rope_paged_prefill_hd256", "k_v_norm_rope_paged_prefill_hd512",
-           "q_norm_rope_prefill_hd512", "psw_rope_tables", "psw_plan_device_errors"]
+           "q_norm_rope_prefill_hd512", "psw_rope_tables", "psw_plan_device_errors",
+           "psw_kv_server_create", "psw_kv_server_destroy", "psw_kv_server_free_pages",
+           "psw_kv_request_create", "psw_kv_request_release", "psw_kv_request_info",
+           "psw_kv_admit", "psw_kv_commit", "psw_kv_abort", "psw_kv_step_tables"]
 
 
 def _check(rc: int):
@@ -285,3 +312,79 @@ def rope_tables(cos_out, sin_out, positions: int, head_dim: int, theta: float,
     """Fill fp32 [positions][head_dim/2] cos/sin tables on the device."""
     _check(_rope(_ptr(cos_out), _ptr(sin_out), int(positions), int(head_dim), float(theta),
                  _stream_handle(stream)))
+
+
+# ------------------------------------------------- two-family page accounting ----
+
+KV_LOCAL, KV_GLOBAL = 0, 1
+
+
+class KvServer:
+    """Page accounting of the two KV families (``psw_kv_*``); host only."""
+
+    def __init__(self, local_pages: int, global_pages: int, local_page_size: int = 16,
+                 global_page_size: int = 16, window_left: int = -1, rope_positions: int = 16384):
+        d = KvServerDesc(int(local_pages), int(global_pages), int(local_page_size),
+                         int(global_page_size), int(window_left), int(rope_positions))
+        h = c_vp()
+        _check(_kv_create(ctypes.byref(d), ctypes.byref(h)))
+        self.handle = h.value
+        self.page_size = (int(local_page_size), int(global_page_size))
+
+    def free_pages(self):
+        lf, gf = c_i64(), c_i64()
+        _check(_kv_free(self.handle, ctypes.byref(lf), ctypes.byref(gf)))
+        return lf.value, gf.value
+
+    def request(self) -> "KvRequest":
+        h = c_vp()
+        _check(_kv_req_create(self.handle, ctypes.byref(h)))
+        return KvRequest(self, h.value)
+
+    def admit(self, req: "KvRequest", n_new: int) -> None:
+        _check(_kv_admit(self.handle, req.handle, int(n_new)))
+
+    def commit(self, req: "KvRequest") -> None:
+        _check(_kv_commit(self.handle, req.handle))
+
+    def abort(self, req: "KvRequest") -> None:
+        _check(_kv_abort(self.handle, req.handle))
+
+    def release(self, req: "KvRequest") -> None:
+        _check(_kv_req_release(self.handle, req.handle))
+        req.handle = None
+
+    def step_tables(self, reqs, family: int):
+        """(qo_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len) of one
+        family for a batch of requests with admitted steps, as int32 numpy arrays."""
+        n = len(reqs)
+        arr = (c_vp * n)(*[r.handle for r in reqs])
+        sts = [r.state() for r in reqs]
+        if family == KV_LOCAL:
+            cap = sum(st.local_held + st.local_reserved for st in sts)
+        else:
+            cap = sum(st.global_held + st.global_reserved for st in sts)
+        cap = max(int(cap), 1)
+        qo = np.zeros(n + 1, np.int32)
+        kvp = np.zeros(n + 1, np.int32)
+        idx = np.zeros(cap, np.int32)
+        last = np.zeros(n, np.int32)
+        p = lambda a: a.ctypes.data_as(c_i32p)
+        _check(_kv_tables(self.handle, arr, n, int(family), p(qo), p(kvp), p(idx), cap, p(last)))
+        return qo, kvp, idx[:kvp[-1]].copy(), last
+
+    def close(self) -> None:
+        if self.handle is not None:
+            _check(_kv_destroy(self.handle))
+            self.handle = None
+
+
+class KvRequest:
+    def __init__(self, server: KvServer, handle):
+        self.server = server
+        self.handle = handle
+
+    def state(self) -> KvRequestState:
+        st = KvRequestState()
+        _check(_kv_req_info(self.handle, ctypes.byref(st)))
+        return st
