@@ -349,6 +349,56 @@ def cpu_baseline(synth, oracle, case, budget_s=12.0):
                       f"(seq_len {lens}), all 16 heads, fp64, {dt:.1f} s"}
 
 
+def decode_sweep():
+    """Split vs direct decode forms over batch x KV length, both families
+    (median of 30 launches each, HIP events around the entry call, merge
+    included); prints a markdown table."""
+    import torch
+    import synth
+    import paged_sliding_window_page_amd as psw
+    dev = torch.device("cuda", 0)
+    print("| family | batch | KV keys | split (us) | direct (us) | faster |")
+    print("|---|---|---|---|---|---|")
+    for hd, geo, wl in ((256, synth.LOCAL, 1023), (512, synth.GLOBAL, -1)):
+        for batch in (1, 8, 64):
+            for kv in (64, 256, 512, 1024, 2048, 8192):
+                case = synth.attention_case(11, [1] * batch, [kv] * batch, fill_pool=False, **geo)
+                pool = torch.randn(case.pool.numel(), device=dev).mul_(0.25).to(torch.bfloat16)
+                q = case.q.to(dev)
+                o = torch.empty(batch, 16, hd, dtype=torch.bfloat16, device=dev)
+                plan = psw.Plan(case.qo_indptr, case.table.kv_page_indptr,
+                                case.table.kv_page_indices, case.table.kv_last_page_len,
+                                num_qo_heads=16, num_kv_heads=geo["num_kv_heads"], head_dim=hd,
+                                page_size=16, num_pages=case.num_pages)
+                pd = psw.pool_desc(pool, num_layers=1, num_pages=case.num_pages, page_size=16,
+                                   num_kv_heads=geo["num_kv_heads"], head_dim=hd)
+                res = []
+                for mode in (psw.DECODE_SPLIT, psw.DECODE_DIRECT):
+                    plan.set_decode_mode(mode)
+
+                    def run():
+                        if hd == 256:
+                            psw.paged_decode_window_hd256(plan, pd, 0, q, 1.0, wl, o)
+                        else:
+                            psw.paged_decode_hd512(plan, pd, 0, q, 1.0, o)
+                    for _ in range(3):
+                        run()
+                    ts = []
+                    for _ in range(30):
+                        a = torch.cuda.Event(enable_timing=True)
+                        b = torch.cuda.Event(enable_timing=True)
+                        a.record()
+                        run()
+                        b.record()
+                        torch.cuda.synchronize()
+                        ts.append(a.elapsed_time(b) * 1e3)
+                    res.append(float(np.median(ts)))
+                plan.close()
+                keys = min(kv, wl + 1) if wl >= 0 else kv
+                print(f"| hd{hd} | {batch} | {keys} | {res[0]:.1f} | {res[1]:.1f} | "
+                      f"{'direct' if res[1] < res[0] else 'split'} |", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -361,11 +411,16 @@ def main():
                          "times: the reference for scaling hardware byte counters")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the traffic summary of two rocprofv3 counter runs and exit")
+    ap.add_argument("--decode-sweep", action="store_true",
+                    help="time the split and direct decode forms over batch x KV length and exit")
     args = ap.parse_args()
     if args.pmc_summary:
         if args.copy_mib <= 0:
             raise SystemExit("--pmc-summary needs the --copy-mib size the runs used")
         print(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.copy_mib), end="")
+        return
+    if args.decode_sweep:
+        decode_sweep()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path; "

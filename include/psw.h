@@ -200,6 +200,38 @@ int paged_prefill_hd512(psw_plan* plan, const psw_pool* pool, int64_t layer,
                         const void* q, float sm_scale, void* o, int32_t o_dtype,
                         psw_stream_t stream);
 
+/* --------------------------------------------------------------- decode ---- */
+
+/* Decode is the prefill contract at qo_len 1 ([P3] Description: decode runs
+ * the prefill entry at one token; the dedicated form is a measured choice).
+ * The prefill entries take it as well; these two require qo_len == 1 for
+ * every request (PSW_E_SHAPE otherwise) and are otherwise identical to
+ * paged_prefill_window_hd256 / paged_prefill_hd512.
+ * Two forms, chosen per call by the plan's decode mode:
+ *   PSW_DECODE_SPLIT   each request's keys cut into splits (about 2048
+ *                      (split, KV head) work-groups per launch), fp32 partial
+ *                      results in the plan's workspace, then a merge launch;
+ *   PSW_DECODE_DIRECT  one work-group per (request, KV head) over all of its
+ *                      keys, writing O itself: no workspace, no merge;
+ *   PSW_DECODE_AUTO    DIRECT while every request reads at most 160 keys
+ *                      (head_dim 256) or 256 keys (head_dim 512), or at most
+ *                      1024 keys once batch x KV heads >= 256 work-groups
+ *                      fill the GPU; SPLIT otherwise (crossovers measured on
+ *                      MI355X: `bench.py --decode-sweep`).
+ * A GQA group of 32 always takes SPLIT. */
+enum { PSW_DECODE_AUTO = 0, PSW_DECODE_SPLIT = 1, PSW_DECODE_DIRECT = 2 };
+int psw_plan_set_decode_mode(psw_plan* plan, int32_t mode);
+/* What the next decode call with this window would launch: *direct = 1 for
+ * the direct form, *work_groups = (split, KV head) work-groups of the decode
+ * launch.  PSW_E_SHAPE when the plan has a request with qo_len > 1. */
+int psw_plan_decode_form(const psw_plan* plan, int64_t window_left, int32_t* direct,
+                         int64_t* work_groups);
+int paged_decode_window_hd256(psw_plan* plan, const psw_pool* pool, int64_t layer,
+                              const void* q, float sm_scale, int64_t window_left, void* o,
+                              int32_t o_dtype, psw_stream_t stream);
+int paged_decode_hd512(psw_plan* plan, const psw_pool* pool, int64_t layer, const void* q,
+                       float sm_scale, void* o, int32_t o_dtype, psw_stream_t stream);
+
 /* ----------------------------------------------------------------- prep ---- */
 
 /* hd256 fused prep ([P2] Proposed Plan), one pass per token:

@@ -109,6 +109,13 @@ _prefill256 = _sig("paged_prefill_window_hd256", ctypes.c_int, c_vp, ctypes.POIN
                    c_i64, c_vp, ctypes.c_float, c_i64, c_vp, c_i32, c_vp)
 _prefill512 = _sig("paged_prefill_hd512", ctypes.c_int, c_vp, ctypes.POINTER(PoolDesc), c_i64,
                    c_vp, ctypes.c_float, c_vp, c_i32, c_vp)
+_decode256 = _sig("paged_decode_window_hd256", ctypes.c_int, c_vp, ctypes.POINTER(PoolDesc),
+                  c_i64, c_vp, ctypes.c_float, c_i64, c_vp, c_i32, c_vp)
+_decode512 = _sig("paged_decode_hd512", ctypes.c_int, c_vp, ctypes.POINTER(PoolDesc), c_i64,
+                  c_vp, ctypes.c_float, c_vp, c_i32, c_vp)
+_decode_mode = _sig("psw_plan_set_decode_mode", ctypes.c_int, c_vp, c_i32)
+_decode_form = _sig("psw_plan_decode_form", ctypes.c_int, c_vp, c_i64, c_i32p,
+                    ctypes.POINTER(c_i64))
 _prep256 = _sig("qkv_norm_rope_paged_prefill_hd256", ctypes.c_int, c_vp, ctypes.POINTER(PoolDesc),
                 c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
                 ctypes.c_float, c_vp, c_vp)
@@ -135,7 +142,8 @@ _dev_err = _sig("psw_plan_device_errors", ctypes.c_int, c_vp)
 # every symbol include/psw.h declares
 EXPORTS = ["psw_last_error", "psw_version", "psw_check_pool", "psw_plan_create",
            "psw_plan_update", "psw_plan_destroy", "psw_plan_get_info", "psw_prefill_tile_q",
-           "paged_prefill_window_hd256", "paged_prefill_hd512",
+           "paged_prefill_window_hd256", "paged_prefill_hd512", "paged_decode_window_hd256",
+           "paged_decode_hd512", "psw_plan_set_decode_mode", "psw_plan_decode_form",
            "qkv_norm_rope_paged_prefill_hd256", "k_v_norm_rope_paged_prefill_hd512",
            "q_norm_rope_prefill_hd512", "psw_rope_tables", "psw_plan_device_errors",
            "psw_kv_server_create", "psw_kv_server_destroy", "psw_kv_server_free_pages",
@@ -235,6 +243,15 @@ class Plan:
         _check(_plan_info(self._h, ctypes.byref(out)))
         return {f: getattr(out, f) for f, _ in PlanInfo._fields_}
 
+    def set_decode_mode(self, mode: int) -> None:
+        _check(_decode_mode(self.handle, int(mode)))
+
+    def decode_form(self, window_left: int = -1):
+        """(direct, work_groups) of the next decode call with this window."""
+        d, wg = c_i32(), c_i64()
+        _check(_decode_form(self.handle, int(window_left), ctypes.byref(d), ctypes.byref(wg)))
+        return bool(d.value), wg.value
+
     def device_errors(self) -> None:
         _check(_dev_err(self._h))
 
@@ -272,6 +289,27 @@ def paged_prefill_hd512(plan: Plan, pool: PoolDesc, layer: int, q, sm_scale: flo
     _check(_prefill512(plan.handle, ctypes.byref(pool), int(layer), _ptr(q), float(sm_scale),
                        _ptr(o), o_dtype,
                        plan.stream if stream is None else _stream_handle(stream)))
+
+
+DECODE_AUTO, DECODE_SPLIT, DECODE_DIRECT = 0, 1, 2
+
+
+def paged_decode_window_hd256(plan: "Plan", pool: PoolDesc, layer: int, q, sm_scale: float,
+                              window_left: int, o, stream=None) -> None:
+    import torch
+    o_dtype = 1 if o.dtype == torch.bfloat16 else 0
+    _check(_decode256(plan.handle, ctypes.byref(pool), int(layer), _ptr(q), float(sm_scale),
+                      int(window_left), _ptr(o), o_dtype,
+                      plan.stream if stream is None else _stream_handle(stream)))
+
+
+def paged_decode_hd512(plan: "Plan", pool: PoolDesc, layer: int, q, sm_scale: float, o,
+                       stream=None) -> None:
+    import torch
+    o_dtype = 1 if o.dtype == torch.bfloat16 else 0
+    _check(_decode512(plan.handle, ctypes.byref(pool), int(layer), _ptr(q), float(sm_scale),
+                      _ptr(o), o_dtype,
+                      plan.stream if stream is None else _stream_handle(stream)))
 
 
 def qkv_norm_rope_paged_prefill_hd256(plan: Plan, pool: PoolDesc, layer: int, q_in, k_in, v_in,

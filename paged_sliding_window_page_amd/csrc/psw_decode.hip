@@ -252,6 +252,24 @@ void decode_kernel(AttnParams P) {
   l_tot += __shfl_xor(l_tot, 32);
   if (!row_valid) return;
   // lane (n, q4), O^T block db, register r: dim dim0 + 16 db + 4 q4 + r of row n
+  if (P.direct_out) {
+    // the split is the whole request: normalise and write O
+    const float inv = 1.0f / l_tot;
+    const int64_t orow = ((int64_t)q_row * P.num_qo_heads + head) * D + dim0 + 4 * q4;
+    if (P.out_bf16) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        bf16x4 v = {(__bf16)(oacc[db][0] * inv), (__bf16)(oacc[db][1] * inv),
+                    (__bf16)(oacc[db][2] * inv), (__bf16)(oacc[db][3] * inv)};
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(P.o) + orow + 16 * db) = v;
+      }
+    } else {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<f32x4*>(static_cast<float*>(P.o) + orow + 16 * db) = oacc[db] * inv;
+    }
+    return;
+  }
   const int64_t base = (int64_t)slot * P.num_qo_heads + head;
   float* po = P.part_o + base * D + dim0 + 4 * q4;
 #pragma unroll

@@ -46,6 +46,8 @@ struct AttnParams {
   int32_t group_shift;  // log2(H_q / H_kv)
   int32_t window_left;  // -1: none
   float scale_log2;     // sm_scale * log2(e)
+  int32_t direct_out;   // decode, one split per request: write O, not partials
+  int32_t out_bf16;     // O element type when direct_out (else fp32)
 };
 
 struct MergeParams {

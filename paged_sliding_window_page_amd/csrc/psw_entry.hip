@@ -32,6 +32,7 @@ struct psw_device_mirror {
   size_t dc_req_cap = 0;
   uint64_t dc_gen = 0;
   int64_t dc_wl = -3;
+  int32_t dc_mode = -1;
   int32_t* prep = nullptr;
   size_t prep_cap = 0;
   uint64_t prep_gen = 0;
@@ -170,14 +171,20 @@ int run_attention(psw_plan* plan, const psw_pool* pool, int64_t layer, const voi
   const int64_t wle = psw::effective_window(st, window_left);
   const bool decode = st.max_qo_len == 1;
   const int kv_tile = psw::kv_tile_for(head_dim);
+  // the group-32 decode runs in the split mode of the attention kernel
+  static_assert(psw::kDecodeKernelMaxGroup == psw_dev::kDecodeMaxGroup, "decode group bound");
+  const int32_t dmode = psw::effective_decode_mode(st, plan->decode_mode);
   if (decode) {
-    if (plan->decode.window_left != wle)
-      psw::build_decode_schedule(st, wle, &plan->decode);
+    if (plan->decode.window_left != wle || plan->decode.mode != dmode)
+      psw::build_decode_schedule(st, wle, dmode, &plan->decode);
   } else {
     if (plan->prefill.window_left != wle)
       psw::build_prefill_schedule(st, wle, kv_tile, &plan->prefill);
   }
 
+  // only the decode kernel writes O itself; every other decode path writes
+  // partials for the merge
+  const bool direct = decode && plan->decode.direct && st.group <= psw_dev::kDecodeMaxGroup;
   hipStream_t s = reinterpret_cast<hipStream_t>(plan->stream);
   rc = ensure_mirror(plan);
   if (rc) return rc;
@@ -185,21 +192,27 @@ int run_attention(psw_plan* plan, const psw_pool* pool, int64_t layer, const voi
   psw_dev::AttnParams p{};
   int n_items = 0;
   if (decode) {
-    if (m->dc_gen != plan->generation || m->dc_wl != wle) {
+    if (m->dc_gen != plan->generation || m->dc_wl != wle || m->dc_mode != dmode) {
       rc = upload(m, &m->dc_items, &m->dc_cap, m->st_dc, plan->decode.items, s);
       if (!rc) rc = upload(m, &m->dc_req, &m->dc_req_cap, m->st_req, plan->decode.req_splits, s);
       if (rc) return rc;
       m->dc_gen = plan->generation;
       m->dc_wl = wle;
+      m->dc_mode = dmode;
     }
-    const size_t part_floats =
-        size_t(plan->decode.num_partials) * st.num_qo_heads * (size_t(head_dim) + 2);
-    rc = ensure(&m->part, &m->part_cap, part_floats * sizeof(float), s);
-    if (rc) return rc;
     p.items = m->dc_items;
-    p.part_o = m->part;
-    p.part_ml = m->part + size_t(plan->decode.num_partials) * st.num_qo_heads * head_dim;
     n_items = plan->decode.num_partials;
+    if (direct) {
+      p.direct_out = 1;
+      p.out_bf16 = o_dtype == 1;
+    } else {
+      const size_t part_floats =
+          size_t(plan->decode.num_partials) * st.num_qo_heads * (size_t(head_dim) + 2);
+      rc = ensure(&m->part, &m->part_cap, part_floats * sizeof(float), s);
+      if (rc) return rc;
+      p.part_o = m->part;
+      p.part_ml = m->part + size_t(plan->decode.num_partials) * st.num_qo_heads * head_dim;
+    }
   } else {
     if (m->pf_gen != plan->generation || m->pf_wl != wle) {
       rc = upload(m, &m->pf_items, &m->pf_cap, m->st_pf, plan->prefill.items, s);
@@ -231,7 +244,7 @@ int run_attention(psw_plan* plan, const psw_pool* pool, int64_t layer, const voi
     e = head_dim == 256 ? psw_dev::launch_attention_d256(decode, o_dtype == 1, p, n_items, s)
                         : psw_dev::launch_attention_d512(decode, o_dtype == 1, p, n_items, s);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
-  if (decode) {
+  if (decode && !direct) {
     psw_dev::MergeParams mp{};
     mp.part_o = p.part_o;
     mp.part_ml = p.part_ml;
@@ -302,6 +315,23 @@ int paged_prefill_window_hd256(psw_plan* plan, const psw_pool* pool, int64_t lay
 
 int paged_prefill_hd512(psw_plan* plan, const psw_pool* pool, int64_t layer, const void* q,
                         float sm_scale, void* o, int32_t o_dtype, psw_stream_t stream) {
+  return run_attention(plan, pool, layer, q, sm_scale, -1, o, o_dtype, stream, 512);
+}
+
+int paged_decode_window_hd256(psw_plan* plan, const psw_pool* pool, int64_t layer, const void* q,
+                              float sm_scale, int64_t window_left, void* o, int32_t o_dtype,
+                              psw_stream_t stream) {
+  psw::clear_error();
+  if (plan && plan->st.max_qo_len != 1)
+    return fail(PSW_E_SHAPE, "decode entries take one query token per request");
+  return run_attention(plan, pool, layer, q, sm_scale, window_left, o, o_dtype, stream, 256);
+}
+
+int paged_decode_hd512(psw_plan* plan, const psw_pool* pool, int64_t layer, const void* q,
+                       float sm_scale, void* o, int32_t o_dtype, psw_stream_t stream) {
+  psw::clear_error();
+  if (plan && plan->st.max_qo_len != 1)
+    return fail(PSW_E_SHAPE, "decode entries take one query token per request");
   return run_attention(plan, pool, layer, q, sm_scale, -1, o, o_dtype, stream, 512);
 }
 

@@ -235,7 +235,11 @@ void build_prefill_schedule(const PlanState& st, int64_t wl, int32_t kv_tile, Pr
   out->total_tiles = total;
 }
 
-void build_decode_schedule(const PlanState& st, int64_t wl, DecodeSchedule* out) {
+int32_t effective_decode_mode(const PlanState& st, int32_t mode) {
+  return st.group > kDecodeKernelMaxGroup ? int32_t(PSW_DECODE_SPLIT) : mode;
+}
+
+void build_decode_schedule(const PlanState& st, int64_t wl, int32_t mode, DecodeSchedule* out) {
   // keys each request must read: the window (or everything) ending at p = kv_len - 1
   std::vector<int64_t> lo(st.batch), n(st.batch);
   int64_t key_heads = 0;
@@ -254,6 +258,17 @@ void build_decode_schedule(const PlanState& st, int64_t wl, DecodeSchedule* out)
   int64_t chunk = (key_heads + kDecodeTargetUnits - 1) / kDecodeTargetUnits;
   chunk = std::max<int64_t>(chunk, 16 * int64_t(st.group));
   chunk = std::max<int64_t>(unit, (chunk + unit - 1) / unit * unit);
+  // Non-partitioned form: one work-group per (request, KV head) reads all of
+  // the request's keys and writes O itself (no partials, no merge launch).
+  int64_t n_max = 0;
+  for (int32_t b = 0; b < st.batch; ++b) n_max = std::max(n_max, n[b]);
+  const bool full_grid = int64_t(st.batch) * st.num_kv_heads >= kDecodeFullGrid;
+  const int64_t direct_keys = full_grid ? kDecodeDirectKeysFull
+                              : st.head_dim == 256 ? kDecodeDirectKeys256
+                                                   : kDecodeDirectKeys512;
+  const bool direct = mode == PSW_DECODE_DIRECT ||
+                      (mode == PSW_DECODE_AUTO && n_max <= direct_keys);
+  if (direct) chunk = std::max<int64_t>(chunk, (n_max + unit - 1) / unit * unit);
   // Each request's keys are cut into ceil(n / chunk) nearly equal splits at
   // multiples of kDecodeSplitUnit (absolute key index, so no KV tile is read
   // by two splits).  Items are then ordered longest first, so the short
@@ -287,7 +302,11 @@ void build_decode_schedule(const PlanState& st, int64_t wl, DecodeSchedule* out)
   for (const Split& sp : splits) out->items.insert(out->items.end(), {sp.b, sp.slot, sp.lo, sp.hi});
   out->num_partials = slot;
   out->window_left = wl;
+  out->mode = mode;
   out->chunk = static_cast<int32_t>(chunk);
+  // the direct form only when it was chosen (a split schedule keeps its
+  // partials and merge even where every request fits one split)
+  out->direct = direct && slot == st.batch;
 }
 
 void build_prep_items(const PlanState& st, std::vector<int32_t>* out) {
@@ -438,6 +457,31 @@ const char* psw_version(void) { return "psw 0.1.0 gfx950"; }
 int psw_check_pool(const psw_pool* pool) {
   psw::clear_error();
   return psw::check_pool(pool, false);
+}
+
+int psw_plan_decode_form(const psw_plan* plan, int64_t window_left, int32_t* direct,
+                         int64_t* work_groups) {
+  psw::clear_error();
+  if (!plan || !direct || !work_groups) return psw::fail(PSW_E_NULL, "plan or output is NULL");
+  const psw::PlanState& st = plan->st;
+  if (st.max_qo_len != 1) return psw::fail(PSW_E_SHAPE, "the plan is not a decode batch");
+  if (window_left < -1) return psw::fail(PSW_E_RANGE, "window_left must be >= -1");
+  psw::DecodeSchedule ds;
+  psw::build_decode_schedule(st, psw::effective_window(st, window_left),
+                             psw::effective_decode_mode(st, plan->decode_mode), &ds);
+  *direct = ds.direct ? 1 : 0;
+  *work_groups = int64_t(ds.num_partials) * st.num_kv_heads;
+  return PSW_OK;
+}
+
+int psw_plan_set_decode_mode(psw_plan* plan, int32_t mode) {
+  psw::clear_error();
+  if (!plan) return psw::fail(PSW_E_NULL, "plan is NULL");
+  if (mode != PSW_DECODE_AUTO && mode != PSW_DECODE_SPLIT && mode != PSW_DECODE_DIRECT)
+    return psw::fail(PSW_E_SHAPE, "decode mode must be PSW_DECODE_AUTO, _SPLIT or _DIRECT");
+  plan->decode_mode = mode;
+  plan->decode.window_left = -2;  // rebuilt by the next decode call
+  return PSW_OK;
 }
 
 int psw_prefill_tile_q(int64_t group, int64_t head_dim, int32_t* tile_q) {

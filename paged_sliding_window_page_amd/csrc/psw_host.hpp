@@ -45,6 +45,16 @@ constexpr int kKvTile512 = 32;             // keys per prefill tile at head_dim 
 constexpr int kDecodeTile = 16;            // keys per decode MFMA step (one wave per split)
 constexpr int kDecodeSplitUnit = 64;       // split boundaries are multiples of this key index
 constexpr int kDecodeTargetUnits = 2048;   // decode (split, KV head) work-groups aimed for
+// Automatic decode form (measured on MI355X, split vs direct over batch x KV
+// length): the direct form wins while its longest work-group loop stays
+// shorter than the split form's extra merge launch -- up to about 160 keys at
+// head_dim 256 and 256 at head_dim 512 -- or, once the direct grid alone
+// fills the 256 CUs, up to 1024 keys.
+constexpr int kDecodeDirectKeys256 = 160;
+constexpr int kDecodeDirectKeys512 = 256;
+constexpr int kDecodeDirectKeysFull = 1024;
+constexpr int kDecodeFullGrid = 256;
+constexpr int kDecodeKernelMaxGroup = 16;  // widest GQA group of the decode kernel
 constexpr int kMaxGroup = 32;
 
 int derive_tile_q(int64_t group, int64_t head_dim, int32_t* tile_q);
@@ -84,12 +94,18 @@ void build_prefill_schedule(const PlanState& st, int64_t window_left, int32_t kv
 // request are consecutive, in key order.
 struct DecodeSchedule {
   int64_t window_left = -2;
+  int32_t mode = -1;                 // PSW_DECODE_* the schedule was built for
   int32_t chunk = 0;                 // keys per split
+  bool direct = false;               // one split per request: O written by the decode kernel
   std::vector<int32_t> items;        // quads
   std::vector<int32_t> req_splits;   // pairs (first partial slot, number of splits) per request
   int32_t num_partials = 0;
 };
-void build_decode_schedule(const PlanState& st, int64_t window_left, DecodeSchedule* out);
+void build_decode_schedule(const PlanState& st, int64_t window_left, int32_t mode,
+                           DecodeSchedule* out);
+// The decode form a plan's mode resolves to: wider groups than the decode
+// kernel's run through the split mode of the attention kernel.
+int32_t effective_decode_mode(const PlanState& st, int32_t mode);
 
 // Prep work items: up to 16 consecutive positions of one request inside one
 // page, as (request, first global token, tokens, page id, first slot, first
@@ -129,6 +145,7 @@ struct psw_plan {
   uint64_t generation = 0;
   psw::PrefillSchedule prefill;
   psw::DecodeSchedule decode;
+  int32_t decode_mode = PSW_DECODE_AUTO;
   std::vector<int32_t> prep_items;
   bool prep_built = false;
   psw_device_mirror* mirror = nullptr;  // created by the first launch

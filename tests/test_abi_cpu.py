@@ -317,6 +317,65 @@ def test_query_prep512_rejects_null_plan_and_hd256_plan():
     assert _code(lambda: _prepq(_plan())) == "PSW_E_PLAN"
 
 
+def test_decode_entries_reject_multi_token_plans_and_bad_modes():
+    plan = _plan()                                  # qo_len 5 and 4
+    pool = _pool()
+    assert _code(lambda: psw._check(psw._decode256(plan.handle, ctypes.byref(pool), 0, FAKE, 1.0,
+                                                   -1, FAKE, 1, 0))) == "PSW_E_SHAPE"
+    assert _code(lambda: plan.set_decode_mode(3)) == "PSW_E_SHAPE"
+    assert _code(lambda: psw._check(psw._decode_mode(None, 0))) == "PSW_E_NULL"
+    plan.set_decode_mode(psw.DECODE_DIRECT)
+    one = _plan(qo_indptr=[0, 1, 2])
+    # validation still runs after the token check: a wrong stream is rejected
+    assert _code(lambda: psw._check(psw._decode256(one.handle, ctypes.byref(pool), 0, FAKE, 1.0,
+                                                   -1, FAKE, 1, 5))) == "PSW_E_PLAN"
+
+
+def _decode_plan(kv, hq, hkv, d):
+    kvp, idx, last, nxt = [0], [], [], 0
+    for k in kv:
+        n = (k + 15) // 16
+        idx += list(range(nxt, nxt + n))
+        nxt += n
+        kvp.append(kvp[-1] + n)
+        last.append(k - (n - 1) * 16)
+    return psw.Plan(list(range(len(kv) + 1)), kvp, idx, last, num_qo_heads=hq, num_kv_heads=hkv,
+                    head_dim=d, page_size=16, num_pages=nxt, stream=0)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(16, 8, 256), (16, 1, 512), (32, 1, 256)])
+def test_decode_form_follows_the_mode(hq, hkv, d):
+    """Split keeps partials even where every request is one split; direct is
+    one work-group per (request, KV head); auto takes direct on short
+    requests; a group of 32 (no direct form) always splits."""
+    short = _decode_plan([40, 700, 129], hq, hkv, d)
+    long_ = _decode_plan([40, 7000, 129], hq, hkv, d)
+    group32 = hq // hkv == 32
+    for plan in (short, long_):
+        plan.set_decode_mode(psw.DECODE_SPLIT)
+        assert plan.decode_form(200)[0] is False
+        plan.set_decode_mode(psw.DECODE_DIRECT)
+        direct, wgs = plan.decode_form(200)
+        assert direct is (not group32)
+        if not group32:
+            assert wgs == 3 * hkv
+    short.set_decode_mode(psw.DECODE_AUTO)
+    assert short.decode_form(100)[0] is (not group32)      # at most 101 keys each
+    assert short.decode_form(-1)[0] is False                # 700 keys
+    long_.set_decode_mode(psw.DECODE_AUTO)
+    assert long_.decode_form(-1)[0] is False
+    assert _code(lambda: _plan().decode_form(-1)) == "PSW_E_SHAPE"
+
+
+def test_decode_auto_form_thresholds():
+    small = lambda kv, d, hkv: _decode_plan(kv, 16, hkv, d).decode_form(-1)[0]
+    assert small([160] * 4, 256, 8) and not small([161] * 4, 256, 8)
+    assert small([256] * 4, 512, 1) and not small([257] * 4, 512, 1)
+    # 32 requests x 8 KV heads = 256 work-groups: direct up to 1024 keys
+    assert small([1024] * 32, 256, 8) and not small([1025] * 32, 256, 8)
+    assert not small([1024] * 31, 256, 8)
+
+
 def test_rope_table_rejects():
     assert _code(lambda: psw.rope_tables(FAKE, FAKE, 0, 256, 1e4, stream=0)) == "PSW_E_SHAPE"
     assert _code(lambda: psw.rope_tables(FAKE, FAKE, 16, 255, 1e4, stream=0)) == "PSW_E_SHAPE"

@@ -111,3 +111,49 @@ def test_decode_full_size_sampled(hd):
     ref = oracle_attention(host, window_left=wl, samples=samples)
     idx = tuple(np.array(samples).T)
     check_close(gpu[idx], ref[idx], f"decode full hd{hd}")
+
+
+def _run_decode_entry(case, mode, window_left, out_dtype):
+    """The dedicated decode entries with the plan's decode form forced."""
+    import paged_sliding_window_page_amd as psw
+    from gpu_util import make_plan, pool_desc_of, to_np64
+    dev = torch.device("cuda", 0)
+    say(f"[gpu] decode entry mode={mode} D={case.head_dim} kv={case.kv_lens[:6]} "
+        f"wl={window_left} out={out_dtype}")
+    pool_d = case.pool.to(dev)
+    q_d = case.q.to(dev)
+    o_d = torch.full((q_d.shape[0], case.num_qo_heads, case.head_dim), float("nan"),
+                     dtype=out_dtype, device=dev)
+    plan = make_plan(case)
+    plan.set_decode_mode(mode)
+    pd = pool_desc_of(case, pool_d)
+    if case.head_dim == 256:
+        psw.paged_decode_window_hd256(plan, pd, case.layer, q_d, 1.0, window_left, o_d)
+    else:
+        psw.paged_decode_hd512(plan, pd, case.layer, q_d, 1.0, o_d)
+    torch.cuda.synchronize()
+    plan.close()
+    return to_np64(o_d)
+
+
+@pytest.mark.parametrize("hd", [256, 512])
+@pytest.mark.parametrize("mode", [0, 1, 2])   # auto, split, direct (one work-group per request)
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_decode_entries_each_form(hd, mode, out_dtype):
+    case = _case(hd, 71, KV_MIX + [512, 513, 4000])
+    wl = 300 if hd == 256 else -1
+    gpu = _run_decode_entry(case, mode, wl, out_dtype)
+    check_close(gpu, oracle_attention(case, window_left=wl), f"decode entry hd{hd} mode {mode}")
+
+
+@pytest.mark.parametrize("hd", [256, 512])
+def test_decode_forms_agree_on_short_requests(hd):
+    """Short requests (the automatic choice takes the direct form): direct and
+    split give the same result within the gate, and both match the oracle."""
+    case = _case(hd, 73, [3, 64, 200, 511, 512] * 4)
+    wl = 1023 if hd == 256 else -1
+    direct = _run_decode_entry(case, 2, wl, torch.float32)
+    split = _run_decode_entry(case, 1, wl, torch.float32)
+    ref = oracle_attention(case, window_left=wl)
+    check_close(direct, ref, "direct")
+    check_close(split, ref, "split")
