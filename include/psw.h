@@ -202,8 +202,9 @@ int paged_prefill_hd512(psw_plan* plan, const psw_pool* pool, int64_t layer,
 
 /* --------------------------------------------------------------- decode ---- */
 
-/* Decode is the prefill contract at qo_len 1 ([P3] Description: decode runs
- * the prefill entry at one token; the dedicated form is a measured choice).
+/* Decode is the prefill contract at qo_len 1 ([P3] Description: one-token
+ * decode is served by the prefill entry, and a dedicated form is left to
+ * measurement).
  * The prefill entries take it as well; these two require qo_len == 1 for
  * every request (PSW_E_SHAPE otherwise) and are otherwise identical to
  * paged_prefill_window_hd256 / paged_prefill_hd512.
@@ -297,9 +298,9 @@ int psw_rope_tables(float* cos_out, float* sin_out, int64_t positions, int64_t h
 /* --------------------------------------------- two-family page accounting ---- */
 
 /* Host-side page accounting for serving from two KV families at once ([P3]
- * Description: a pool per family, a per-request state in each, admission that
- * keeps the two pools consistent; [P3] review thread: the KV frontier moves
- * only after a successful step).  No device memory is involved: the server
+ * Description: each family has its own pool and each request its own state
+ * in both, and admitting a step must leave the two pools in agreement; [P3]
+ * review thread: the KV frontier moves only after a successful step).  No device memory is involved: the server
  * hands out page ids of the two caller-owned pools (psw_pool), and
  * psw_kv_step_tables turns a batch of admitted steps into the CSR metadata of
  * psw_plan_desc.  Not thread-safe: one host thread drives a server.
@@ -310,8 +311,8 @@ int psw_rope_tables(float* cos_out, float* sin_out, int64_t positions, int64_t h
  *                  this server, no step is pending, the held pages match F,
  *                  F + n <= rope_positions, and F + n <= window_left + 1 when
  *                  window_left >= 0 (slots equal absolute positions only
- *                  until the window starts dropping keys; this path refuses
- *                  to cross it).  Then it reserves ceil((F+n)/P_f) - held_f
+ *                  until the window starts dropping keys, so a step that
+ *                  would go past the window is refused).  Then it reserves ceil((F+n)/P_f) - held_f
  *                  pages of both families; if either pool is short, nothing
  *                  is kept: both pools end exactly as they were (the same free
  *                  ids in the same order) and PSW_E_RANGE is returned.

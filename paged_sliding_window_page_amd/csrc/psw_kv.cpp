@@ -188,7 +188,7 @@ int psw_kv_admit(psw_kv_server* s, psw_kv_request* r, int64_t n_new) {
     return fail(PSW_E_RANGE, "position " + std::to_string(post - 1) + " is past the " +
                                  std::to_string(s->rope_positions) + " RoPE positions");
   // cache slots equal absolute positions only while no query can lose a key to
-  // the window; this path refuses to cross it
+  // the window; a step past it is refused
   if (s->window_left >= 0 && post > s->window_left + 1)
     return fail(PSW_E_RANGE, "KV length " + std::to_string(post) +
                                  " would cross the local window of " +

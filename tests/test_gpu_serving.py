@@ -2,7 +2,7 @@
 with page tables issued by the two-family accounting, on cuda:0.
 
 Contract (PR "feat(gemma4): paged KV serving across both attention families",
-Description): a pool per family and a request holding pages in both; each
+Description): each family with its own pool, a request holding pages in both; each
 step's prep writes the new tokens at their absolute positions through the
 step's tables and attention reads the whole KV back; decode is the prefill
 entry at one token; the frontier moves only after the step.  Checked per step
