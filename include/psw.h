@@ -300,7 +300,7 @@ int psw_rope_tables(float* cos_out, float* sin_out, int64_t positions, int64_t h
 /* Host-side page accounting for serving from two KV families at once ([P3]
  * Description: each family has its own pool and each request its own state
  * in both, and admitting a step must leave the two pools in agreement; [P3]
- * review thread: the KV frontier moves only after a successful step).  No device memory is involved: the server
+ * review thread: the KV frontier moves once the step has succeeded).  No device memory is involved: the server
  * hands out page ids of the two caller-owned pools (psw_pool), and
  * psw_kv_step_tables turns a batch of admitted steps into the CSR metadata of
  * psw_plan_desc.  Not thread-safe: one host thread drives a server.

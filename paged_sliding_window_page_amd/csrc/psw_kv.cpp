@@ -2,7 +2,7 @@
 // from: one page pool per family, a per-request state in each, and step
 // admission that is atomic across both (PR "feat(gemma4): paged KV serving
 // across both attention families", Description; its review thread for
-// committing the frontier only after a successful step).  No HIP API is used
+// committing the frontier once the step has succeeded).  No HIP API is used
 // here; everything runs, and is tested, on the CPU.
 //
 // Model.  A request has one frontier F (its KV length, the same in both
@@ -78,7 +78,7 @@ using psw::fail;
 int check_pair(const psw_kv_server* s, const psw_kv_request* r) {
   if (!s) return fail(PSW_E_NULL, "server is NULL");
   if (!r) return fail(PSW_E_NULL, "request is NULL");
-  // page ids only mean something against the pools that issued them
+  // a page id is meaningful only for the pool it came from
   if (r->owner != s) return fail(PSW_E_PLAN, "request belongs to another server");
   return PSW_OK;
 }
@@ -196,7 +196,7 @@ int psw_kv_admit(psw_kv_server* s, psw_kv_request* r, int64_t n_new) {
   int64_t need[2];
   for (int f = 0; f < 2; ++f)
     need[f] = ceil_div(post, s->pool[f].page_size) - static_cast<int64_t>(r->held[f].size());
-  // both reservations before either is committed; a refused side drops the other
+  // take both sides first; if the second side is short, hand the first back
   std::vector<int32_t> got[2];
   if (!s->pool[PSW_KV_LOCAL].take(need[PSW_KV_LOCAL], &got[PSW_KV_LOCAL]))
     return fail(PSW_E_RANGE, "local pool has " +

@@ -1,14 +1,14 @@
 """Two-family page accounting on the host (no GPU).
 
 Contract (PR "feat(gemma4): paged KV serving across both attention families",
-Description and Verification; its review thread on committing the frontier
-after a successful step): one pool per family, the page count of a step is
-the ceiling over the post-step KV length minus what the request holds, both
-reservations are taken before either is committed and a refused side drops
-the other so both pools end at their pre-request occupancy, nothing changes
-state before a step is admissible (window and RoPE bounds, matching
-frontiers), page ids belong to the server that issued them, and the frontier
-moves only on commit.
+Description and Verification; its review thread on when the frontier may
+move): each family has its own pool; a step needs the ceiling of its
+post-step KV length over the page size, less the pages already held; both
+families are reserved before anything is kept, and when one side cannot be
+granted the other is handed back, leaving both pools as they were; every
+bound (window, RoPE tables, matching frontiers) is checked before any state
+changes; a request is only valid against its own server; the frontier moves
+on commit and nowhere else.
 """
 import math
 
