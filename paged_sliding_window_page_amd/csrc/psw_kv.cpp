@@ -1,6 +1,6 @@
 // Host-side page accounting of the two KV families a two-family model serves
-// from: one page pool per family, a per-request state in each, and step
-// admission that is atomic across both (PR "feat(gemma4): paged KV serving
+// from: each family has its own page pool, each request its own state in
+// both, and a step is admitted for both families or for neither (PR "feat(gemma4): paged KV serving
 // across both attention families", Description; its review thread for
 // committing the frontier once the step has succeeded).  No HIP API is used
 // here; everything runs, and is tested, on the CPU.
