@@ -128,7 +128,22 @@ typedef struct {
   int64_t tile_q_override;          /* 0: derive tile_q; else the plan records
                                        this value and prefill entries whose
                                        compiled tile differs reject the plan     */
+  const int32_t* kv_len;            /* optional [batch]: absolute KV lengths, for
+                                       resident windows (below); NULL: each is
+                                       (n_pages - 1) * page_size + last_page_len */
 } psw_plan_desc;
+
+/* Resident windows (a ring of pages per request).  With kv_len given, a
+ * request whose kv_len exceeds n_pages * page_size keeps only its last
+ * R = n_pages * page_size positions: position p lives in page
+ * kv_page_indices[kv_page_indptr[b] + (p / page_size) % n_pages], slot
+ * p % page_size, so cache slots and absolute positions differ once the window
+ * has wrapped ([P2] Proposed Plan: callers past the window need a slot map).
+ * Positions, masks and RoPE stay absolute.  kv_last_page_len must then be
+ * (kv_len - 1) % page_size + 1, and a request that does not wrap must have
+ * exactly its derived kv_len.  Attention rejects (PSW_E_RANGE) a wrapped
+ * request whose ring could miss a key its queries see: no window, or
+ * R < window_left + qo_len; the prep rejects a step longer than its ring. */
 
 /* Opaque plan: validated host copy of the metadata, the recorded bounds
  * (max page id, max last-page length), the tile decision and work lists, and a

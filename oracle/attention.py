@@ -14,7 +14,13 @@ attention families", Description):
       0 <= p_i - j <= window_left      (window_left >= 0; inclusive distance)
       0 <= p_i - j                     (window_left == -1; full causal)
 
-  so a query sees at most window_left + 1 keys and always sees itself.  With
+  so a query sees at most window_left + 1 keys and always sees itself.
+  kv_len_b is the absolute KV length: from the pages by default, or given
+  explicitly for a resident window, whose pages hold only the last
+  n_pages * page_size positions as a ring (position p in page (p // P) mod
+  n_pages; issue "gemma4: serving prep needs pool-write forms", Proposed
+  Plan: past the window, slots and positions need a separate map).  A query
+  that would see a key the ring no longer holds is an error.  With
   s_j = sm_scale * <q_i,h , K_j,g>, the output is sum_j softmax(s)_j V_j,g,
   softmax in base e over the allowed keys only.  sm_scale is whatever the caller
   passes (the model runs unscaled attention, sm_scale = 1).
@@ -31,7 +37,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .layout import PoolGeometry, kv_blocks, gather_kv, kv_lengths
+from .layout import PoolGeometry, kv_blocks, gather_kv, kv_lengths, resident_start
 from .bf16 import to_f64
 
 
@@ -61,7 +67,7 @@ def attention_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, pos: np.nda
 
 def paged_attention(q, pool, geom: PoolGeometry, layer: int, qo_indptr, kv_page_indptr,
                     kv_page_indices, kv_last_page_len, sm_scale: float, window_left: int,
-                    requests=None, samples=None) -> np.ndarray:
+                    requests=None, samples=None, kv_len=None) -> np.ndarray:
     """float64 output [sum(qo), H_q, D].
 
     q: bf16 tensor / uint16 bits / float array [sum(qo), H_q, D].
@@ -69,6 +75,8 @@ def paged_attention(q, pool, geom: PoolGeometry, layer: int, qo_indptr, kv_page_
     requests: optional subset of request indices to compute (others stay NaN).
     samples: optional list of (token_index, head) pairs; only those rows are
         computed (others stay NaN).
+    kv_len: optional absolute KV lengths (resident windows); default from the
+        pages and last-page lengths.
     """
     qf = to_f64(q)
     n_tok, h_q, d = qf.shape
@@ -82,7 +90,9 @@ def paged_attention(q, pool, geom: PoolGeometry, layer: int, qo_indptr, kv_page_
     qo_indptr = np.asarray(qo_indptr, dtype=np.int64)
     kv_page_indptr = np.asarray(kv_page_indptr, dtype=np.int64)
     kv_page_indices = np.asarray(kv_page_indices, dtype=np.int64)
-    kv_len = kv_lengths(kv_page_indptr, kv_last_page_len, geom.page_size)
+    if kv_len is None:
+        kv_len = kv_lengths(kv_page_indptr, kv_last_page_len, geom.page_size)
+    kv_len = np.asarray(kv_len, dtype=np.int64)
     batch = len(qo_indptr) - 1
     out = np.full((n_tok, h_q, d), np.nan)
 
@@ -104,6 +114,11 @@ def paged_attention(q, pool, geom: PoolGeometry, layer: int, qo_indptr, kv_page_
         pages = kv_page_indices[kv_page_indptr[b]:kv_page_indptr[b + 1]]
         k, v = gather_kv(kblk, vblk, layer, pages, n_kv, geom.page_size)
         start = n_kv - qo_len
+        first = resident_start(len(pages), n_kv, geom.page_size)
+        if first > 0:
+            seen = allowed_keys(start + np.arange(qo_len, dtype=np.int64), n_kv, window_left)
+            if seen[:, :first].any():
+                raise ValueError(f"request {b}: a query sees a key the ring no longer holds")
         if want is None:
             pos = start + np.arange(qo_len, dtype=np.int64)
             for h in range(h_q):

@@ -70,16 +70,30 @@ def kv_lengths(kv_page_indptr, kv_last_page_len, page_size: int) -> np.ndarray:
     return (n - 1) * page_size + last
 
 
+def resident_start(n_pages: int, kv_len: int, page_size: int) -> int:
+    """First absolute position a request's pages still hold: 0 while they
+    cover every position, else kv_len - n_pages * page_size (a resident
+    window keeps only the last n_pages * page_size positions)."""
+    return max(0, int(kv_len) - int(n_pages) * int(page_size))
+
+
 def gather_kv(kblk: np.ndarray, vblk: np.ndarray, layer: int, page_ids, kv_len: int,
               page_size: int):
     """Logical K and V of one request, float64 [kv_len, H_kv, D] each.
 
-    Key j is read from page page_ids[j // page_size], slot j % page_size."""
+    Key j is read from page page_ids[(j // page_size) % n_pages], slot
+    j % page_size: the plain table while the pages cover all kv_len positions,
+    the slot map of a resident window (a ring of the request's pages) once
+    kv_len exceeds them.  Keys before ``resident_start`` are no longer held;
+    their rows come back as zeros and callers must not use them."""
     page_ids = np.asarray(page_ids, dtype=np.int64)
     j = np.arange(kv_len, dtype=np.int64)
-    page = page_ids[j // page_size]
+    page = page_ids[(j // page_size) % len(page_ids)]
     slot = j % page_size
     # advanced indices around a slice: the gathered key axis comes first
-    k = kblk[layer, page, :, slot, :]          # [kv_len, H, D]
-    v = vblk[layer, page, :, :, slot]          # [kv_len, H, D]
-    return bits_to_f64(k), bits_to_f64(v)
+    k = bits_to_f64(kblk[layer, page, :, slot, :])     # [kv_len, H, D]
+    v = bits_to_f64(vblk[layer, page, :, :, slot])     # [kv_len, H, D]
+    gone = j < resident_start(len(page_ids), kv_len, page_size)
+    k[gone] = 0.0
+    v[gone] = 0.0
+    return k, v

@@ -58,10 +58,13 @@ def rope_rotate_half(y: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray
     return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
 
 
-def token_positions(qo_indptr, kv_page_indptr, kv_last_page_len, page_size: int) -> np.ndarray:
-    """Absolute position of every token: start_pos_b + t, start_pos_b = kv_len_b - qo_len_b."""
+def token_positions(qo_indptr, kv_page_indptr, kv_last_page_len, page_size: int,
+                    kv_len=None) -> np.ndarray:
+    """Absolute position of every token: start_pos_b + t, start_pos_b = kv_len_b - qo_len_b
+    (kv_len from the pages, or given for resident windows)."""
     qo_indptr = np.asarray(qo_indptr, dtype=np.int64)
-    kv_len = kv_lengths(kv_page_indptr, kv_last_page_len, page_size)
+    if kv_len is None:
+        kv_len = kv_lengths(kv_page_indptr, kv_last_page_len, page_size)
     pos = np.empty(int(qo_indptr[-1]), dtype=np.int64)
     for b in range(len(qo_indptr) - 1):
         q0, q1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
@@ -103,9 +106,11 @@ def q_prep_hd512(q_in, q_norm_w, pos, eps: float, theta: float):
 
 
 def expected_pool_writes(geom: PoolGeometry, layer: int, qo_indptr, kv_page_indptr,
-                         kv_page_indices, kv_last_page_len):
-    """For every token, the (page, slot) it is written to in ``layer``."""
-    pos = token_positions(qo_indptr, kv_page_indptr, kv_last_page_len, geom.page_size)
+                         kv_page_indices, kv_last_page_len, kv_len=None):
+    """For every token, the (page, slot) it is written to in ``layer``: position
+    p in page ids[(p // P) mod n_pages] (the plain table, or a resident
+    window's ring), slot p mod P."""
+    pos = token_positions(qo_indptr, kv_page_indptr, kv_last_page_len, geom.page_size, kv_len)
     qo_indptr = np.asarray(qo_indptr, dtype=np.int64)
     kv_page_indptr = np.asarray(kv_page_indptr, dtype=np.int64)
     ids = np.asarray(kv_page_indices, dtype=np.int64)
@@ -113,7 +118,7 @@ def expected_pool_writes(geom: PoolGeometry, layer: int, qo_indptr, kv_page_indp
     for b in range(len(qo_indptr) - 1):
         q0, q1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
         pages = ids[kv_page_indptr[b]:kv_page_indptr[b + 1]]
-        page[q0:q1] = pages[pos[q0:q1] // geom.page_size]
+        page[q0:q1] = pages[(pos[q0:q1] // geom.page_size) % len(pages)]
     slot = pos % geom.page_size
     return page, slot
 

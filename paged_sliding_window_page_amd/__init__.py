@@ -66,7 +66,8 @@ class PlanDesc(ctypes.Structure):
     _fields_ = [("batch", c_i64), ("qo_indptr", c_i32p), ("kv_page_indptr", c_i32p),
                 ("kv_page_indices", c_i32p), ("kv_last_page_len", c_i32p),
                 ("num_qo_heads", c_i64), ("num_kv_heads", c_i64), ("head_dim", c_i64),
-                ("page_size", c_i64), ("num_pages", c_i64), ("tile_q_override", c_i64)]
+                ("page_size", c_i64), ("num_pages", c_i64), ("tile_q_override", c_i64),
+                ("kv_len", c_i32p)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -210,32 +211,36 @@ class Plan:
 
     def __init__(self, qo_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len, *,
                  num_qo_heads, num_kv_heads, head_dim, page_size, num_pages,
-                 tile_q_override=0, stream=None, batch=None):
+                 tile_q_override=0, stream=None, batch=None, kv_len=None):
         self._h = c_vp()
         self.stream = _stream_handle(stream) if stream != "none" else None
         desc, keep = self._desc(qo_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len,
                                 num_qo_heads, num_kv_heads, head_dim, page_size, num_pages,
-                                tile_q_override, batch)
+                                tile_q_override, batch, kv_len)
         _check(_plan_create(ctypes.byref(desc), self.stream, ctypes.byref(self._h)))
 
     @staticmethod
     def _desc(qo_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
-              num_kv_heads, head_dim, page_size, num_pages, tile_q_override, batch):
+              num_kv_heads, head_dim, page_size, num_pages, tile_q_override, batch, kv_len=None):
         arrs = [_i32(qo_indptr), _i32(kv_page_indptr), _i32(kv_page_indices),
                 _i32(kv_last_page_len)]
         if batch is None:
             batch = len(arrs[0]) - 1
         ptrs = [a.ctypes.data_as(c_i32p) if a.size else ctypes.cast(None, c_i32p) for a in arrs]
+        kvl = None if kv_len is None else _i32(kv_len)
+        if kvl is not None:
+            arrs.append(kvl)
         desc = PlanDesc(int(batch), *ptrs, int(num_qo_heads), int(num_kv_heads), int(head_dim),
-                        int(page_size), int(num_pages), int(tile_q_override))
+                        int(page_size), int(num_pages), int(tile_q_override),
+                        kvl.ctypes.data_as(c_i32p) if kvl is not None else ctypes.cast(None, c_i32p))
         return desc, arrs
 
     def update(self, qo_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len, *,
                num_qo_heads, num_kv_heads, head_dim, page_size, num_pages, tile_q_override=0,
-               batch=None):
+               batch=None, kv_len=None):
         desc, keep = self._desc(qo_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len,
                                 num_qo_heads, num_kv_heads, head_dim, page_size, num_pages,
-                                tile_q_override, batch)
+                                tile_q_override, batch, kv_len)
         _check(_plan_update(self._h, ctypes.byref(desc)))
 
     def info(self) -> dict:

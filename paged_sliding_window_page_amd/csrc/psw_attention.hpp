@@ -225,12 +225,13 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
   // cache.
   constexpr int NPG = KT / 8;  // most pages a tile can touch (page_size >= 8)
   constexpr int NPP = PAGE16 ? KT / 16 : 1;
-  auto page_id = [&](int j0, int p) { return ldu(pages + min((j0 >> pshift) + p, last_page)); };
+  const PageRing ring = page_ring(last_page + 1, kvl, pshift);
+  auto page_id = [&](int j0, int p) { return ldu(pages + ring((j0 >> pshift) + p)); };
   auto load_pids = [&](int tv, int tk) {  // tile indices of the V and K tiles
     int r = 0;
     if (lane < 2 * NPG) {
       const int jt = (jt0 + (lane < NPG ? tv : tk)) * KT;
-      r = pages[min((jt >> pshift) + (lane & (NPG - 1)), last_page)];
+      r = pages[ring((jt >> pshift) + (lane & (NPG - 1)))];
     }
     return r;
   };

@@ -105,7 +105,9 @@ void decode_kernel(AttnParams P) {
   const int pshift = P.ps.page_shift;
   const int pmask = P.ps.page_size - 1;
   const int psize = P.ps.page_size;
-  const int last_pidx = k_hi >> pshift;  // last page the split may touch
+  // page list index of an absolute page (resident windows wrap the list)
+  const PageRing ring = page_ring(ldu(P.kv_page_indptr + b + 1) - ldu(P.kv_page_indptr + b),
+                                  ldu(P.kv_len + b), pshift);
   // Tile-relative key of the K row this lane feeds into S^T block sb: block sb,
   // output row 4 q + r holds key 8 q + 4 sb + r, so the lane of row n reads key
   // 8 (n / 4) + 4 sb + n % 4.  Its V^T operand covers keys 8 q4 .. 8 q4 + 7.
@@ -116,15 +118,15 @@ void decode_kernel(AttnParams P) {
   // byte addresses of one tile's K rows (block 0 / 1) and this lane's V^T chunk
   auto tile_addr = [&](int j0, const char** kp0, const char** kp1, const char** vp) {
     if constexpr (PMODE == 2) {
-      const int64_t pg = (int64_t)ldu(pages + (j0 >> pshift)) * page_bytes;
+      const int64_t pg = (int64_t)ldu(pages + ring(j0 >> pshift)) * page_bytes;
       const int in_page = j0 & pmask;
       *kp0 = kbase + pg + (int64_t)(in_page + kkey0) * D * 2 + kdim_off;
       *kp1 = *kp0 + 4 * D * 2;
       *vp = vbase + pg + (in_page + 8 * q4) * 2 + vdim_off;
     } else if constexpr (PMODE == 1) {
       const int pi = j0 >> 4;
-      const int64_t pa = (int64_t)ldu(pages + pi) * page_bytes;
-      const int64_t pb = (int64_t)ldu(pages + min(pi + 1, last_pidx)) * page_bytes;
+      const int64_t pa = (int64_t)ldu(pages + ring(pi)) * page_bytes;
+      const int64_t pb = (int64_t)ldu(pages + ring(pi + 1)) * page_bytes;
       // keys 0..15 of the tile sit in page a, 16..31 in page b
       const int64_t kpg = kkey0 < 16 ? pa : pb;
       *kp0 = kbase + kpg + (int64_t)(kkey0 & 15) * D * 2 + kdim_off;
@@ -132,9 +134,9 @@ void decode_kernel(AttnParams P) {
       *vp = vbase + (q4 < 2 ? pa : pb) + ((8 * q4) & 15) * 2 + vdim_off;
     } else {
       const int k0 = j0 + kkey0, k1 = k0 + 4, kv = j0 + 8 * q4;
-      const int64_t p0 = pages[min(k0 >> pshift, last_pidx)];
-      const int64_t p1 = pages[min(k1 >> pshift, last_pidx)];
-      const int64_t pv = pages[min(kv >> pshift, last_pidx)];
+      const int64_t p0 = pages[ring(k0 >> pshift)];
+      const int64_t p1 = pages[ring(k1 >> pshift)];
+      const int64_t pv = pages[ring(kv >> pshift)];
       *kp0 = kbase + p0 * page_bytes + (int64_t)(k0 & pmask) * D * 2 + kdim_off;
       *kp1 = kbase + p1 * page_bytes + (int64_t)(k1 & pmask) * D * 2 + kdim_off;
       *vp = vbase + pv * page_bytes + (kv & pmask) * 2 + vdim_off;

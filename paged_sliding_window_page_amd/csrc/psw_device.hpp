@@ -50,6 +50,28 @@ struct AttnParams {
   int32_t out_bf16;     // O element type when direct_out (else fp32)
 };
 
+// Page list index of an absolute page index a = key / page_size of one
+// request.  The list holds n pages; when kv_len exceeds them it is a ring that
+// keeps the last n * page_size positions, page a at index a % n.  Indices are
+// first clamped into the resident span [lo, hi] (loads past either end read
+// some resident page; the caller masks those keys), then mapped without a
+// division: base is the multiple of n at or below hi.
+struct PageRing {
+  int n, lo, hi, base;
+  __device__ __forceinline__ int operator()(int a) const {
+    const int c = min(max(a, lo), hi);
+    return c - base + (c < base ? n : 0);
+  }
+};
+__device__ __forceinline__ PageRing page_ring(int n_pages, int kv_len, int page_shift) {
+  PageRing r;
+  r.n = n_pages;
+  r.hi = (kv_len - 1) >> page_shift;
+  r.lo = max(0, kv_len - (n_pages << page_shift)) >> page_shift;
+  r.base = (r.hi / n_pages) * n_pages;
+  return r;
+}
+
 struct MergeParams {
   const float* part_o;
   const float* part_ml;

@@ -166,9 +166,23 @@ int build_state(const psw_plan_desc* d, PlanState* out) {
       return fail(PSW_E_RANGE, "last_page_len " + std::to_string(last) + " of request " +
                                    std::to_string(b) + " is outside [1, page_size]");
     const int64_t n_pages = int64_t(s.kv_page_indptr[b + 1]) - s.kv_page_indptr[b];
-    const int64_t kv = (n_pages - 1) * int64_t(s.page_size) + last;
+    int64_t kv = (n_pages - 1) * int64_t(s.page_size) + last;
     if (!fits_i32(kv))
       return fail(PSW_E_OVERFLOW, "kv_len of request " + std::to_string(b) + " is past INT32_MAX");
+    if (d->kv_len) {
+      // absolute length: equal to the derived one unless the pages wrap
+      const int64_t given = d->kv_len[b];
+      if (given <= n_pages * s.page_size) {
+        if (given != kv)
+          return fail(PSW_E_SHAPE, "kv_len of request " + std::to_string(b) +
+                                       " disagrees with its pages and last_page_len");
+      } else if (last != (given - 1) % s.page_size + 1) {
+        return fail(PSW_E_SHAPE, "last_page_len of wrapped request " + std::to_string(b) +
+                                     " must be (kv_len - 1) % page_size + 1");
+      }
+      kv = given;
+      s.any_ring = s.any_ring || given > n_pages * s.page_size;
+    }
     const int32_t qo = s.qo_indptr[b + 1] - s.qo_indptr[b];
     if (kv < qo)
       return fail(PSW_E_SHAPE, "request " + std::to_string(b) + " has kv_len < qo_len");
@@ -190,7 +204,8 @@ int build_state(const psw_plan_desc* d, PlanState* out) {
   const int32_t scalars[] = {s.batch, s.num_qo_heads, s.num_kv_heads, s.head_dim, s.page_size,
                              s.num_pages, s.tile_q, s.max_page_id, s.max_last_page_len};
   h = fnv1a(h, scalars, sizeof(scalars));
-  for (const auto* v : {&s.qo_indptr, &s.kv_page_indptr, &s.kv_page_indices, &s.last_page_len})
+  for (const auto* v :
+       {&s.qo_indptr, &s.kv_page_indptr, &s.kv_page_indices, &s.last_page_len, &s.kv_len})
     h = fnv1a(h, v->data(), v->size() * sizeof(int32_t));
   s.digest = h;
   *out = std::move(s);
@@ -319,7 +334,7 @@ void build_prep_items(const PlanState& st, std::vector<int32_t>* out) {
       const int32_t pos = start + t;
       const int32_t slot = pos & (st.page_size - 1);
       const int32_t n = std::min({qo - t, st.page_size - slot, 16});
-      const int32_t page = st.kv_page_indices[st.kv_page_indptr[b] + pos / st.page_size];
+      const int32_t page = st.page_of(b, pos);
       out->insert(out->end(), {b, st.qo_indptr[b] + t, n, page, slot, pos});
       t += n;
     }
@@ -374,6 +389,22 @@ int check_attention_call(const psw_plan* plan, const psw_pool* pool, int64_t lay
   if (!checked_mul(int64_t(s.total_qo), s.num_qo_heads, &rows) ||
       !checked_mul(rows, s.head_dim, &rows))
     return fail(PSW_E_OVERFLOW, "q/o size overflows int64");
+  // a wrapped ring holds the last n_pages * page_size positions: every key a
+  // query of the call sees must be among them
+  if (s.any_ring) {
+    for (int32_t b = 0; b < s.batch; ++b) {
+      if (!s.wraps(b)) continue;
+      const int64_t ring = int64_t(s.n_pages(b)) * s.page_size;
+      const int64_t qo = s.qo_indptr[b + 1] - s.qo_indptr[b];
+      if (window_left < 0 || ring < window_left + qo)
+        return fail(PSW_E_RANGE, "request " + std::to_string(b) + " has a ring of " +
+                                     std::to_string(ring) + " slots, too few for " +
+                                     (window_left < 0 ? std::string("attention without a window")
+                                                      : "window " + std::to_string(window_left) +
+                                                            " and " + std::to_string(qo) +
+                                                            " queries"));
+    }
+  }
   return PSW_OK;
 }
 
@@ -415,11 +446,15 @@ int check_prep_call(const psw_plan* plan, const psw_pool* pool, int64_t layer,
     const int32_t qo = s.qo_indptr[b + 1] - s.qo_indptr[b];
     const int64_t start = int64_t(s.kv_len[b]) - qo;
     const int64_t n_pages = int64_t(s.kv_page_indptr[b + 1]) - s.kv_page_indptr[b];
-    if (n_pages * s.page_size < start + qo)
+    if (!s.wraps(b) && n_pages * s.page_size < start + qo)
       return fail(PSW_E_RANGE, "pages of request " + std::to_string(b) +
                                    " do not cover its positions");
+    if (qo > n_pages * s.page_size)
+      return fail(PSW_E_RANGE, "request " + std::to_string(b) + " writes " + std::to_string(qo) +
+                                   " positions into a ring of " +
+                                   std::to_string(n_pages * s.page_size) + " slots");
     for (int64_t pg = start / s.page_size; pg <= (start + qo - 1) / s.page_size; ++pg) {
-      const int32_t id = s.kv_page_indices[s.kv_page_indptr[b] + pg];
+      const int32_t id = s.page_of(b, pg * s.page_size);
       if (!written.insert(id).second)
         return fail(PSW_E_SHAPE, "page " + std::to_string(id) +
                                      " would be written twice by this prep call");

@@ -70,7 +70,15 @@ struct PlanState {
   int32_t max_qo_len = 0, max_kv_len = 0;
   int32_t max_page_id = -1, max_last_page_len = 0;
   std::vector<int32_t> qo_indptr, kv_page_indptr, kv_page_indices, last_page_len, kv_len;
+  bool any_ring = false;  // some request's pages wrap (resident window)
   uint64_t digest = 0;
+
+  int32_t n_pages(int32_t b) const { return kv_page_indptr[b + 1] - kv_page_indptr[b]; }
+  bool wraps(int32_t b) const { return int64_t(kv_len[b]) > int64_t(n_pages(b)) * page_size; }
+  // page id holding absolute position p of request b (ring or not)
+  int32_t page_of(int32_t b, int64_t p) const {
+    return kv_page_indices[kv_page_indptr[b] + (p / page_size) % n_pages(b)];
+  }
 };
 
 // Builds and validates a complete PlanState from a description; *out is only

@@ -164,7 +164,8 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   // A tile is 16 load instructions of 1 KiB; instruction `ins` covers K keys
   // 2 ins, 2 ins + 1 and V^T chunks (k8 = ins / 4, d = 64 (ins % 4) + lane).
   // Wave wg of the loading group issues instructions 4 r + wg, r < 4.
-  auto page_id = [&](int idx) __attribute__((always_inline)) { return ldu(pages + min(idx, last_page)); };
+  const PageRing ring = page_ring(last_page + 1, kvl, PAGE16 ? 4 : P.ps.page_shift);
+  auto page_id = [&](int idx) __attribute__((always_inline)) { return ldu(pages + ring(idx)); };
 
   // ---- LDS operand addresses (as in attention_kernel, 32-key tiles) ----
   const int krow = kperm(n);

@@ -94,6 +94,21 @@ def random_page_table(kv_lens, page_size: int, num_pages: int, gen: torch.Genera
     return PageTable(lengths_to_indptr(n_pages), indices, last)
 
 
+def ring_page_table(kv_lens, ring_pages, page_size: int, num_pages: int,
+                    gen: torch.Generator) -> PageTable:
+    """Resident-window tables: request b holds min(ceil(kv_len_b / P), ring_pages[b])
+    distinct random pages; when kv_len_b is larger the pages are a ring and
+    the last-page length is that of position kv_len_b - 1."""
+    n_pages = [min((int(n) + page_size - 1) // page_size, int(r)) for n, r in zip(kv_lens, ring_pages)]
+    need = sum(n_pages)
+    if need > num_pages:
+        raise ValueError(f"pool of {num_pages} pages cannot hold {need}")
+    perm = torch.randperm(num_pages, generator=gen)
+    indices = perm[:need].to(torch.int32).numpy().copy()
+    last = np.array([(int(n) - 1) % page_size + 1 for n in kv_lens], dtype=np.int32)
+    return PageTable(lengths_to_indptr(n_pages), indices, last)
+
+
 @dataclass
 class AttentionCase:
     """One batch for a paged attention entry, all tensors on the CPU."""

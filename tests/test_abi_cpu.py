@@ -381,3 +381,47 @@ def test_rope_table_rejects():
     assert _code(lambda: psw.rope_tables(FAKE, FAKE, 16, 255, 1e4, stream=0)) == "PSW_E_SHAPE"
     assert _code(lambda: psw.rope_tables(FAKE, FAKE, 16, 256, -1.0, stream=0)) == "PSW_E_SCALE"
     assert _code(lambda: psw.rope_tables(None, FAKE, 16, 256, 1e4, stream=0)) == "PSW_E_NULL"
+
+
+# ------------------------------------------------------ resident windows ----
+
+def _ring_plan(kv_len, qo=(5, 4), pages=([3, 1], [0]), last=None, hkv=8, d=256):
+    kvp = [0]
+    idx = []
+    for p in pages:
+        idx += list(p)
+        kvp.append(kvp[-1] + len(p))
+    if last is None:
+        last = [(k - 1) % 16 + 1 for k in kv_len]
+    qo_indptr = [0]
+    for n in qo:
+        qo_indptr.append(qo_indptr[-1] + n)
+    return psw.Plan(qo_indptr, kvp, idx, last, num_qo_heads=16, num_kv_heads=hkv, head_dim=d,
+                    page_size=16, num_pages=4, stream=0, kv_len=kv_len)
+
+
+def test_ring_plan_checks_absolute_lengths():
+    p = _ring_plan([100, 16])                 # request 0 wraps its 2 pages
+    assert p.info()["max_kv_len"] == 100
+    # a request that does not wrap must keep its derived length
+    assert _code(lambda: _ring_plan([100, 15], last=[4, 16])) == "PSW_E_SHAPE"
+    # a wrapped one must carry the slot of its last position
+    assert _code(lambda: _ring_plan([100, 16], last=[16, 16])) == "PSW_E_SHAPE"
+    assert _code(lambda: _ring_plan([3, 16], qo=(5, 4), last=[3, 16])) == "PSW_E_SHAPE"  # kv < qo
+
+
+def test_ring_attention_needs_the_window_inside_the_ring():
+    pool = _pool()
+    plan = _ring_plan([100, 16])              # ring of 32 slots, 5 queries
+    assert _code(lambda: _attn(plan, pool, wl=-1)) == "PSW_E_RANGE"    # no window
+    assert _code(lambda: _attn(plan, pool, wl=28)) == "PSW_E_RANGE"    # 28 + 5 > 32
+    # the global family has no window: a wrapped request is refused
+    p512 = _ring_plan([100, 16], hkv=1, d=512)
+    pool512 = _pool(num_kv_heads=1, head_dim=512)
+    assert _code(lambda: psw.paged_prefill_hd512(p512, pool512, 0, _T(), 1.0, _T(),
+                                                 stream=0)) == "PSW_E_RANGE"
+
+
+def test_ring_prep_refuses_a_step_longer_than_its_ring():
+    plan = _ring_plan([100, 16], qo=(40, 4))  # 40 positions into 32 slots
+    assert _code(lambda: _prep(plan, _pool(), positions=128)) == "PSW_E_RANGE"

@@ -297,3 +297,61 @@ def test_rejects_bad_window():
                                 page_size=2, num_pages=1)
     with pytest.raises(ValueError):
         _run(case, window_left=-2)
+
+
+# ------------------------------------------------------ resident windows ----
+
+def _ring_fixture(seed, kv, qo, ring_pages, window_left, page_size=16, heads=(4, 2), d=32):
+    """An unwrapped pool holding positions 0..kv-1 and a ring of ring_pages
+    pages holding the last ring_pages * P of them, copied position by position
+    with this test's own index formula (ring page (p // P) mod n, slot p mod P)."""
+    rng = np.random.default_rng(seed)
+    hq, hkv = heads
+    n_full = (kv + page_size - 1) // page_size
+    num_pages = n_full + ring_pages
+    g = oracle.PoolGeometry(1, num_pages, hkv, page_size, d)
+    bits = oracle.f64_to_bf16_bits(rng.normal(0, 0.5, g.numel))
+    kb, vb = oracle.kv_blocks(bits, g)
+    full_ids = np.arange(n_full)
+    ring_ids = n_full + rng.permutation(ring_pages)
+    first = kv - ring_pages * page_size
+    for p in range(max(first, 0), kv):
+        src, dst = full_ids[p // page_size], ring_ids[(p // page_size) % ring_pages]
+        kb[0, dst, :, p % page_size, :] = kb[0, src, :, p % page_size, :]
+        vb[0, dst, :, :, p % page_size] = vb[0, src, :, :, p % page_size]
+    q = oracle.f64_to_bf16_bits(rng.normal(0, 0.5, (qo, hq, d)))
+    return g, bits, q, full_ids, ring_ids
+
+
+@pytest.mark.parametrize("kv,qo,ring,wl", [(300, 40, 10, 100), (300, 1, 8, 127), (1000, 17, 9, 120),
+                                           (160, 20, 10, 140)])
+def test_ring_attention_equals_the_unwrapped_cache(kv, qo, ring, wl):
+    g, bits, q, full_ids, ring_ids = _ring_fixture(kv + qo, kv, qo, ring, wl)
+    n_full = len(full_ids)
+    full = oracle.paged_attention(q, bits, g, 0, [0, qo], [0, n_full], full_ids,
+                                  [kv - (n_full - 1) * 16], 0.3, wl)
+    wrapped = oracle.paged_attention(q, bits, g, 0, [0, qo], [0, ring], ring_ids,
+                                     [(kv - 1) % 16 + 1], 0.3, wl, kv_len=[kv])
+    np.testing.assert_allclose(wrapped, full, rtol=0, atol=1e-14)
+
+
+def test_ring_refuses_a_key_it_no_longer_holds():
+    g, bits, q, _, ring_ids = _ring_fixture(5, 300, 40, 10, 100)
+    with pytest.raises(ValueError):      # window 121 + 40 queries need 161 > 160 slots
+        oracle.paged_attention(q, bits, g, 0, [0, 40], [0, 10], ring_ids, [12], 1.0, 121,
+                               kv_len=[300])
+    with pytest.raises(ValueError):      # no window at all
+        oracle.paged_attention(q, bits, g, 0, [0, 40], [0, 10], ring_ids, [12], 1.0, -1,
+                               kv_len=[300])
+
+
+def test_ring_placement_of_prep_writes():
+    """Positions 290..309 of a 10-page ring land in ring page (p // 16) mod 10,
+    slot p mod 16."""
+    g = oracle.PoolGeometry(2, 40, 1, 16, 8)
+    ids = np.array([7, 3, 31, 0, 12, 5, 9, 22, 18, 1])
+    page, slot = oracle.expected_pool_writes(g, 1, [0, 20], [0, 10], ids, [(310 - 1) % 16 + 1],
+                                             kv_len=[310])
+    p = np.arange(290, 310)
+    np.testing.assert_array_equal(page, ids[(p // 16) % 10])
+    np.testing.assert_array_equal(slot, p % 16)
