@@ -137,8 +137,8 @@ typedef struct {
  * request whose kv_len exceeds n_pages * page_size keeps only its last
  * R = n_pages * page_size positions: position p lives in page
  * kv_page_indices[kv_page_indptr[b] + (p / page_size) % n_pages], slot
- * p % page_size, so cache slots and absolute positions differ once the window
- * has wrapped ([P2] Proposed Plan: callers past the window need a slot map).
+ * p % page_size: once the ring has wrapped, a position and its cache slot
+ * differ ([P2] Proposed Plan: callers past the window need a slot map).
  * Positions, masks and RoPE stay absolute.  kv_last_page_len must then be
  * (kv_len - 1) % page_size + 1, and a request that does not wrap must have
  * exactly its derived kv_len.  Attention rejects (PSW_E_RANGE) a wrapped

@@ -3,8 +3,8 @@
 Contract: once a request's absolute KV length exceeds its pages, the pages
 hold only its last n_pages * page_size positions, position p in page
 (p // P) mod n_pages, slot p mod P (issue "gemma4: serving prep needs
-pool-write forms", Proposed Plan: past the window, cache slots and absolute
-positions need a separate map).  Masks and RoPE stay absolute.  Checked
+pool-write forms", Proposed Plan: once the window has wrapped, a position
+and its cache slot differ and need their own map).  Masks and RoPE stay absolute.  Checked
 against the fp64 oracle, whose ring map is pinned on the CPU against an
 unwrapped copy of the same cache: windowed prefill and decode (both forms)
 over wrapped and unwrapped requests in one batch, and the prep writing a
