@@ -335,7 +335,13 @@ int psw_rope_tables(float* cos_out, float* sin_out, int64_t positions, int64_t h
  *                  ones and F += n.
  *   psw_kv_abort   after a failed step: the reserved pages go back, F stays.
  * Page ids are handed out lowest first from a fresh pool, and a pool's free
- * list is last-in first-out. */
+ * list is last-in first-out.
+ * With local_ring_pages = R_p > 0 the local family instead keeps at most R_p
+ * pages per request (a resident window, see psw_plan_desc.kv_len): it holds
+ * min(ceil(F / P), R_p) pages; a step that ends past R_p * P positions needs
+ * R_p * P >= window_left + n (window_left >= 0), and its tokens overwrite the
+ * oldest slots of the same pages; the window bound above then no longer
+ * applies. */
 enum { PSW_KV_LOCAL = 0, PSW_KV_GLOBAL = 1 };
 
 typedef struct {
@@ -343,6 +349,10 @@ typedef struct {
   int64_t local_page_size, global_page_size;    /* slots per page                 */
   int64_t window_left;                          /* local window (inclusive), -1 */
   int64_t rope_positions;                       /* positions the RoPE tables hold */
+  int64_t local_ring_pages;                     /* 0: no ring (refuse to pass the
+                                                   window); else the local family
+                                                   keeps at most this many pages
+                                                   per request, as a ring       */
 } psw_kv_server_desc;
 
 typedef struct psw_kv_server psw_kv_server;     /* opaque: the two pools         */
@@ -374,14 +384,16 @@ int psw_kv_commit(psw_kv_server* server, psw_kv_request* request);
 int psw_kv_abort(psw_kv_server* server, psw_kv_request* request);
 /* CSR tables of one family for a batch of requests that each have a step
  * pending: request b's queries are its n_b new tokens, its pages the held then
- * the reserved ones, its KV length F_b + n_b.  Host arrays: qo_indptr and
- * kv_page_indptr [n_reqs + 1], kv_last_page_len [n_reqs], kv_page_indices of
- * indices_cap entries (PSW_E_SHAPE when too small).  Also rejects a request
- * listed twice, one without a pending step, and one of another server. */
+ * the reserved ones (a ring's order once it wraps), its KV length F_b + n_b.
+ * Host arrays: qo_indptr and kv_page_indptr [n_reqs + 1], kv_last_page_len
+ * and kv_len [n_reqs] (the plan's optional absolute lengths, needed once a
+ * ring wraps), kv_page_indices of indices_cap entries (PSW_E_SHAPE when too
+ * small).  Also rejects a request listed twice, one without a pending step,
+ * and one of another server. */
 int psw_kv_step_tables(const psw_kv_server* server, psw_kv_request* const* requests,
                        int64_t n_reqs, int32_t family, int32_t* qo_indptr,
                        int32_t* kv_page_indptr, int32_t* kv_page_indices,
-                       int64_t indices_cap, int32_t* kv_last_page_len);
+                       int64_t indices_cap, int32_t* kv_last_page_len, int32_t* kv_len);
 
 /* ----------------------------------------------------------- device check ---- */
 

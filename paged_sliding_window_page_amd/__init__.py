@@ -81,7 +81,8 @@ class PlanInfo(ctypes.Structure):
 
 class KvServerDesc(ctypes.Structure):
     _fields_ = [("local_pages", c_i64), ("global_pages", c_i64), ("local_page_size", c_i64),
-                ("global_page_size", c_i64), ("window_left", c_i64), ("rope_positions", c_i64)]
+                ("global_page_size", c_i64), ("window_left", c_i64), ("rope_positions", c_i64),
+                ("local_ring_pages", c_i64)]
 
 
 class KvRequestState(ctypes.Structure):
@@ -136,7 +137,7 @@ _kv_admit = _sig("psw_kv_admit", ctypes.c_int, c_vp, c_vp, c_i64)
 _kv_commit = _sig("psw_kv_commit", ctypes.c_int, c_vp, c_vp)
 _kv_abort = _sig("psw_kv_abort", ctypes.c_int, c_vp, c_vp)
 _kv_tables = _sig("psw_kv_step_tables", ctypes.c_int, c_vp, ctypes.POINTER(c_vp), c_i64, c_i32,
-                  c_i32p, c_i32p, c_i32p, c_i64, c_i32p)
+                  c_i32p, c_i32p, c_i32p, c_i64, c_i32p, c_i32p)
 _rope = _sig("psw_rope_tables", ctypes.c_int, c_vp, c_vp, c_i64, c_i64, ctypes.c_double, c_vp)
 _dev_err = _sig("psw_plan_device_errors", ctypes.c_int, c_vp)
 
@@ -366,9 +367,11 @@ class KvServer:
     """Page accounting of the two KV families (``psw_kv_*``); host only."""
 
     def __init__(self, local_pages: int, global_pages: int, local_page_size: int = 16,
-                 global_page_size: int = 16, window_left: int = -1, rope_positions: int = 16384):
+                 global_page_size: int = 16, window_left: int = -1, rope_positions: int = 16384,
+                 local_ring_pages: int = 0):
         d = KvServerDesc(int(local_pages), int(global_pages), int(local_page_size),
-                         int(global_page_size), int(window_left), int(rope_positions))
+                         int(global_page_size), int(window_left), int(rope_positions),
+                         int(local_ring_pages))
         h = c_vp()
         _check(_kv_create(ctypes.byref(d), ctypes.byref(h)))
         self.handle = h.value
@@ -398,8 +401,9 @@ class KvServer:
         req.handle = None
 
     def step_tables(self, reqs, family: int):
-        """(qo_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len) of one
-        family for a batch of requests with admitted steps, as int32 numpy arrays."""
+        """(qo_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len, kv_len)
+        of one family for a batch of requests with admitted steps, int32 numpy
+        arrays (kv_len: the plan's absolute lengths)."""
         n = len(reqs)
         arr = (c_vp * n)(*[r.handle for r in reqs])
         sts = [r.state() for r in reqs]
@@ -412,9 +416,11 @@ class KvServer:
         kvp = np.zeros(n + 1, np.int32)
         idx = np.zeros(cap, np.int32)
         last = np.zeros(n, np.int32)
+        kvl = np.zeros(n, np.int32)
         p = lambda a: a.ctypes.data_as(c_i32p)
-        _check(_kv_tables(self.handle, arr, n, int(family), p(qo), p(kvp), p(idx), cap, p(last)))
-        return qo, kvp, idx[:kvp[-1]].copy(), last
+        _check(_kv_tables(self.handle, arr, n, int(family), p(qo), p(kvp), p(idx), cap, p(last),
+                          p(kvl)))
+        return qo, kvp, idx[:kvp[-1]].copy(), last, kvl
 
     def close(self) -> None:
         if self.handle is not None:

@@ -51,15 +51,22 @@ struct PagePool {
   }
 };
 
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
 }  // namespace
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct psw_kv_server {
   PagePool pool[2];  // PSW_KV_LOCAL, PSW_KV_GLOBAL
   int64_t window_left = -1;
   int64_t rope_positions = 0;
+  int64_t ring_pages = 0;  // local family: 0 = no ring
   int64_t live_requests = 0;
+
+  // pages family f holds at frontier F
+  int64_t pages_at(int f, int64_t F) const {
+    const int64_t full = ceil_div(F, pool[f].page_size);
+    return f == PSW_KV_LOCAL && ring_pages > 0 ? std::min(full, ring_pages) : full;
+  }
 };
 
 struct psw_kv_request {
@@ -107,11 +114,16 @@ int psw_kv_server_create(const psw_kv_server_desc* d, psw_kv_server** out) {
     return fail(PSW_E_OVERFLOW, "a pool extent or rope_positions is past INT32_MAX");
   if (d->window_left < -1) return fail(PSW_E_RANGE, "window_left must be >= -1");
   if (d->rope_positions < 1) return fail(PSW_E_SHAPE, "rope_positions must be >= 1");
+  if (d->local_ring_pages < 0 || !psw::fits_i32(d->local_ring_pages))
+    return fail(PSW_E_RANGE, "local_ring_pages must be in [0, INT32_MAX]");
+  if (d->local_ring_pages > 0 && d->window_left < 0)
+    return fail(PSW_E_RANGE, "a local ring needs a window (window_left >= 0)");
   auto s = std::make_unique<psw_kv_server>();
   s->pool[PSW_KV_LOCAL].init(d->local_pages, d->local_page_size);
   s->pool[PSW_KV_GLOBAL].init(d->global_pages, d->global_page_size);
   s->window_left = d->window_left;
   s->rope_positions = d->rope_positions;
+  s->ring_pages = d->local_ring_pages;
   *out = s.release();
   return PSW_OK;
 }
@@ -180,22 +192,30 @@ int psw_kv_admit(psw_kv_server* s, psw_kv_request* r, int64_t n_new) {
   const int64_t post = r->frontier + n_new;
   if (!psw::fits_i32(post)) return fail(PSW_E_OVERFLOW, "KV length after the step is past INT32_MAX");
   for (int f = 0; f < 2; ++f) {
-    if (static_cast<int64_t>(r->held[f].size()) != ceil_div(r->frontier, s->pool[f].page_size))
+    if (static_cast<int64_t>(r->held[f].size()) != s->pages_at(f, r->frontier))
       return fail(PSW_E_SHAPE, std::string(f == PSW_KV_LOCAL ? "local" : "global") +
                                    " pages held do not match the frontier");
   }
   if (post > s->rope_positions)
     return fail(PSW_E_RANGE, "position " + std::to_string(post - 1) + " is past the " +
                                  std::to_string(s->rope_positions) + " RoPE positions");
-  // cache slots equal absolute positions only while no query can lose a key to
-  // the window; a step past it is refused
-  if (s->window_left >= 0 && post > s->window_left + 1)
+  if (s->ring_pages > 0) {
+    // once the ring wraps it must hold every key the step's queries see
+    const int64_t ring = s->ring_pages * s->pool[PSW_KV_LOCAL].page_size;
+    if (post > ring && ring < s->window_left + n_new)
+      return fail(PSW_E_RANGE, "a step of " + std::to_string(n_new) +
+                                   " tokens does not fit the local ring with window " +
+                                   std::to_string(s->window_left));
+  } else if (s->window_left >= 0 && post > s->window_left + 1) {
+    // without a ring, cache slots equal absolute positions only while no query
+    // can lose a key to the window; a step past it is refused
     return fail(PSW_E_RANGE, "KV length " + std::to_string(post) +
                                  " would cross the local window of " +
                                  std::to_string(s->window_left + 1) + " keys");
+  }
   int64_t need[2];
   for (int f = 0; f < 2; ++f)
-    need[f] = ceil_div(post, s->pool[f].page_size) - static_cast<int64_t>(r->held[f].size());
+    need[f] = s->pages_at(f, post) - static_cast<int64_t>(r->held[f].size());
   // take both sides first; if the second side is short, hand the first back
   std::vector<int32_t> got[2];
   if (!s->pool[PSW_KV_LOCAL].take(need[PSW_KV_LOCAL], &got[PSW_KV_LOCAL]))
@@ -248,9 +268,10 @@ int psw_kv_abort(psw_kv_server* s, psw_kv_request* r) {
 int psw_kv_step_tables(const psw_kv_server* s, psw_kv_request* const* reqs, int64_t n_reqs,
                        int32_t family, int32_t* qo_indptr, int32_t* kv_page_indptr,
                        int32_t* kv_page_indices, int64_t indices_cap,
-                       int32_t* kv_last_page_len) {
+                       int32_t* kv_last_page_len, int32_t* kv_len) {
   psw::clear_error();
-  if (!s || !reqs || !qo_indptr || !kv_page_indptr || !kv_page_indices || !kv_last_page_len)
+  if (!s || !reqs || !qo_indptr || !kv_page_indptr || !kv_page_indices || !kv_last_page_len ||
+      !kv_len)
     return fail(PSW_E_NULL, "a server, request list or output array is NULL");
   int rc = check_family(family);
   if (rc) return rc;
@@ -281,10 +302,10 @@ int psw_kv_step_tables(const psw_kv_server* s, psw_kv_request* const* reqs, int6
     for (int32_t id : r->held[family]) kv_page_indices[pi++] = id;
     for (int32_t id : r->reserved[family]) kv_page_indices[pi++] = id;
     const int64_t kv = r->frontier + r->pending_n;
-    const int64_t np = static_cast<int64_t>(r->held[family].size() + r->reserved[family].size());
     qo_indptr[b + 1] = static_cast<int32_t>(qo_indptr[b] + r->pending_n);
     kv_page_indptr[b + 1] = static_cast<int32_t>(pi);
-    kv_last_page_len[b] = static_cast<int32_t>(kv - (np - 1) * psz);
+    kv_last_page_len[b] = static_cast<int32_t>((kv - 1) % psz + 1);
+    kv_len[b] = static_cast<int32_t>(kv);
   }
   return PSW_OK;
 }

@@ -69,7 +69,7 @@ def test_two_families_prefill_then_decode():
         for fam, geo in FAM.items():
             d, hkv = geo["d"], geo["hkv"]
             g = _geom(fam)
-            qo, kvp, idx, last = srv.step_tables(reqs, fam)
+            qo, kvp, idx, last, _ = srv.step_tables(reqs, fam)
             say(f"[gpu] serving step {step} family {d}: qo {np.diff(qo).tolist()} "
                 f"pages {np.diff(kvp).tolist()}")
             plan = psw.Plan(qo, kvp, idx, last, num_qo_heads=16, num_kv_heads=hkv, head_dim=d,
@@ -121,4 +121,47 @@ def test_two_families_prefill_then_decode():
     for r in reqs:
         srv.release(r)
     assert srv.free_pages() == (PAGES, PAGES)
+    srv.close()
+
+
+def test_local_family_runs_past_its_window_through_a_ring():
+    """The local family with a ring of 10 pages (160 slots) and window 127:
+    a 100-token prefill, four 20-token steps (the KV runs to 180 and wraps),
+    then two decode steps, each written by the prep through the step's tables
+    and read back by windowed attention; every step against the oracle."""
+    srv = psw.KvServer(64, 64, window_left=127, rope_positions=512, local_ring_pages=10)
+    r = srv.request()
+    wq = synth.normal_bf16((256,), 0.1, synth.generator(940), mean=1.0)
+    wk = synth.normal_bf16((256,), 0.1, synth.generator(941), mean=1.0)
+    c, s = _tables(512, 256)
+    g = oracle.PoolGeometry(1, 64, 8, 16, 256)
+    pool = torch.full((g.numel,), SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    pd = psw.pool_desc(pool, num_layers=1, num_pages=64, page_size=16, num_kv_heads=8,
+                       head_dim=256)
+    for step, n in enumerate([100, 20, 20, 20, 20, 1, 1]):
+        srv.admit(r, n)
+        qo, kvp, idx, last, kvl = srv.step_tables([r], psw.KV_LOCAL)
+        say(f"[gpu] ring serving step {step}: n={n} kv={int(kvl[0])} pages={int(kvp[-1])}")
+        gen = synth.generator(950 + step)
+        q_in = synth.normal_bf16((n, 16, 256), 1.0, gen)
+        k_in = synth.normal_bf16((n, 8, 256), 1.0, gen)
+        v_in = synth.normal_bf16((n, 8, 256), 1.0, gen)
+        plan = psw.Plan(qo, kvp, idx, last, num_qo_heads=16, num_kv_heads=8, head_dim=256,
+                        page_size=16, num_pages=64, kv_len=kvl)
+        q_out = torch.empty(n, 16, 256, dtype=torch.bfloat16, device=DEV)
+        psw.qkv_norm_rope_paged_prefill_hd256(plan, pd, 0, q_in.to(DEV), k_in.to(DEV),
+                                              v_in.to(DEV), wq.to(DEV), wk.to(DEV), c, s, 1e-6,
+                                              q_out)
+        o = torch.full((n, 16, 256), float("nan"), dtype=torch.bfloat16, device=DEV)
+        psw.paged_prefill_window_hd256(plan, pd, 0, q_out, 1.0, 127, o)
+        torch.cuda.synchronize()
+        plan.device_errors()
+        plan.close()
+        after = pool.view(torch.int16).cpu().numpy().view(np.uint16)
+        ref = oracle.paged_attention(q_out.cpu(), after, g, 0, qo, kvp, idx, last, 1.0, 127,
+                                     kv_len=kvl)
+        check_close(to_np64(o), ref, f"ring serving step {step}")
+        srv.commit(r)
+    assert r.state().frontier == 182 and r.state().local_held == 10
+    srv.release(r)
     srv.close()

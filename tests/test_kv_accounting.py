@@ -31,7 +31,7 @@ def _server(**kw):
 
 
 def _tables(srv, reqs, fam):
-    return srv.step_tables(reqs, fam)
+    return srv.step_tables(reqs, fam)[:4]
 
 
 def test_admit_commit_counts_pages_as_ceilings():
@@ -219,3 +219,39 @@ def test_batch_tables_are_valid_plan_metadata():
         srv.release(r)
     assert srv.free_pages() == (200, 200)
     srv.close()
+
+
+def test_local_ring_keeps_at_most_its_pages():
+    """With a local ring of 4 pages (64 slots) and window 31 the local family
+    stops growing at 4 pages and the KV length runs past the window; the
+    global family keeps every page."""
+    srv = _server(window_left=31, local_ring_pages=4)
+    r = srv.request()
+    srv.admit(r, 40)
+    assert (r.state().local_reserved, r.state().global_reserved) == (3, 3)
+    srv.commit(r)
+    srv.admit(r, 30)                                  # post 70: local 4 (ring), global 5
+    assert (r.state().local_reserved, r.state().global_reserved) == (1, 2)
+    qo, kvp, idx, last, kvl = srv.step_tables([r], psw.KV_LOCAL)
+    assert list(kvl) == [70] and list(last) == [(70 - 1) % 16 + 1] and kvp[-1] == 4
+    plan = psw.Plan(qo, kvp, idx, last, num_qo_heads=16, num_kv_heads=8, head_dim=256,
+                    page_size=16, num_pages=64, stream=0, kv_len=kvl)
+    assert plan.info()["max_kv_len"] == 70
+    plan.close()
+    srv.commit(r)
+    srv.admit(r, 30)                                  # post 100: no new local page
+    assert (r.state().local_reserved, r.state().global_reserved) == (0, 2)
+    srv.commit(r)
+    assert (r.state().frontier, r.state().local_held, r.state().global_held) == (100, 4, 7)
+    # window 31 + 34 queries need 65 slots: the ring holds 64
+    assert _code(lambda: srv.admit(r, 34)) == "PSW_E_RANGE"
+    srv.admit(r, 33)
+    srv.abort(r)
+    srv.release(r)
+    assert srv.free_pages() == (64, 64)
+    srv.close()
+
+
+def test_local_ring_needs_a_window():
+    assert _code(lambda: _server(window_left=-1, local_ring_pages=4)) == "PSW_E_RANGE"
+    assert _code(lambda: _server(window_left=10, local_ring_pages=-1)) == "PSW_E_RANGE"
