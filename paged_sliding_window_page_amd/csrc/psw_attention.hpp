@@ -615,6 +615,7 @@ __global__ __launch_bounds__(D / 4) void merge_kernel(MergeParams P) {
   const int head = blockIdx.x - b * P.num_qo_heads;
   const int first = P.req_splits[2 * b];
   const int ns = P.req_splits[2 * b + 1];
+  if (ns == 0) return;  // the decode kernel wrote this request's O itself
   // Splits are combined 8 at a time with all their loads issued first, so the
   // loop runs at memory throughput rather than one load latency per split.
   constexpr int U = 8;

@@ -39,6 +39,7 @@ struct AttnParams {
   const int32_t* kv_page_indices;
   const int32_t* kv_len;
   const int32_t* items;
+  const int32_t* wg_items;  // decode kernel: items of work-group g are [wg_items[g], wg_items[g+1])
   PoolStrides ps;
   int64_t layer_off;
   int32_t num_qo_heads;
@@ -46,8 +47,7 @@ struct AttnParams {
   int32_t group_shift;  // log2(H_q / H_kv)
   int32_t window_left;  // -1: none
   float scale_log2;     // sm_scale * log2(e)
-  int32_t direct_out;   // decode, one split per request: write O, not partials
-  int32_t out_bf16;     // O element type when direct_out (else fp32)
+  int32_t out_bf16;     // decode kernel: O element type of whole-request items (else fp32)
 };
 
 // Page list index of an absolute page index a = key / page_size of one
@@ -75,7 +75,7 @@ __device__ __forceinline__ PageRing page_ring(int n_pages, int kv_len, int page_
 struct MergeParams {
   const float* part_o;
   const float* part_ml;
-  const int32_t* req_splits;  // pairs (first slot, count)
+  const int32_t* req_splits;  // pairs (first slot, count); count 0: O already written
   const int32_t* qo_indptr;
   void* o;
   int32_t num_qo_heads;
@@ -95,6 +95,7 @@ struct PrepParams {
   __bf16* pool;
   int32_t* err;
   const int32_t* items;
+  const int32_t* wg_items;  // decode kernel: items of work-group g are [wg_items[g], wg_items[g+1])
   PoolStrides ps;
   int64_t layer_off;
   int32_t num_qo_heads;
@@ -112,10 +113,11 @@ hipError_t launch_attention_d256(bool split, bool out_bf16, const AttnParams& p,
                                  hipStream_t s);
 hipError_t launch_attention_d512(bool split, bool out_bf16, const AttnParams& p, int n_items,
                                  hipStream_t s);
-// One-token decode split kernel: one wave per (split, KV head); writes the same
-// partials as the split attention kernels.  Needs H_q / H_kv <= kDecodeMaxGroup.
+// One-token decode kernel: n_wgs = work-groups x KV heads, each work-group
+// running its items (whole requests write O, pieces write the same partials
+// as the split attention kernels).  Needs H_q / H_kv <= kDecodeMaxGroup.
 constexpr int kDecodeMaxGroup = 16;
-hipError_t launch_decode(int head_dim, const AttnParams& p, int n_units, hipStream_t s);
+hipError_t launch_decode(int head_dim, const AttnParams& p, int n_wgs, hipStream_t s);
 hipError_t launch_merge_d256(bool out_bf16, const MergeParams& p, int batch, hipStream_t s);
 hipError_t launch_merge_d512(bool out_bf16, const MergeParams& p, int batch, hipStream_t s);
 hipError_t launch_prep_hd256(const PrepParams& p, int n_items, hipStream_t s);

@@ -182,9 +182,6 @@ int run_attention(psw_plan* plan, const psw_pool* pool, int64_t layer, const voi
       psw::build_prefill_schedule(st, wle, kv_tile, &plan->prefill);
   }
 
-  // only the decode kernel writes O itself; every other decode path writes
-  // partials for the merge
-  const bool direct = decode && plan->decode.direct && st.group <= psw_dev::kDecodeMaxGroup;
   hipStream_t s = reinterpret_cast<hipStream_t>(plan->stream);
   rc = ensure_mirror(plan);
   if (rc) return rc;
@@ -193,7 +190,10 @@ int run_attention(psw_plan* plan, const psw_pool* pool, int64_t layer, const voi
   int n_items = 0;
   if (decode) {
     if (m->dc_gen != plan->generation || m->dc_wl != wle || m->dc_mode != dmode) {
-      rc = upload(m, &m->dc_items, &m->dc_cap, m->st_dc, plan->decode.items, s);
+      // items, then the work-groups' item offsets
+      std::vector<int32_t> table(plan->decode.items);
+      table.insert(table.end(), plan->decode.wg_items.begin(), plan->decode.wg_items.end());
+      rc = upload(m, &m->dc_items, &m->dc_cap, m->st_dc, table, s);
       if (!rc) rc = upload(m, &m->dc_req, &m->dc_req_cap, m->st_req, plan->decode.req_splits, s);
       if (rc) return rc;
       m->dc_gen = plan->generation;
@@ -201,11 +201,10 @@ int run_attention(psw_plan* plan, const psw_pool* pool, int64_t layer, const voi
       m->dc_mode = dmode;
     }
     p.items = m->dc_items;
-    n_items = plan->decode.num_partials;
-    if (direct) {
-      p.direct_out = 1;
-      p.out_bf16 = o_dtype == 1;
-    } else {
+    p.wg_items = m->dc_items + plan->decode.items.size();
+    p.out_bf16 = o_dtype == 1;
+    n_items = static_cast<int>(plan->decode.items.size() / 4);
+    if (plan->decode.num_partials > 0) {
       const size_t part_floats =
           size_t(plan->decode.num_partials) * st.num_qo_heads * (size_t(head_dim) + 2);
       rc = ensure(&m->part, &m->part_cap, part_floats * sizeof(float), s);
@@ -239,12 +238,12 @@ int run_attention(psw_plan* plan, const psw_pool* pool, int64_t layer, const voi
   p.scale_log2 = sm_scale * 1.4426950408889634f;
   hipError_t e;
   if (decode && st.group <= psw_dev::kDecodeMaxGroup)
-    e = psw_dev::launch_decode(head_dim, p, n_items * st.num_kv_heads, s);
+    e = psw_dev::launch_decode(head_dim, p, plan->decode.num_wgs * st.num_kv_heads, s);
   else
     e = head_dim == 256 ? psw_dev::launch_attention_d256(decode, o_dtype == 1, p, n_items, s)
                         : psw_dev::launch_attention_d512(decode, o_dtype == 1, p, n_items, s);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
-  if (decode && !direct) {
+  if (decode && plan->decode.num_partials > 0) {
     psw_dev::MergeParams mp{};
     mp.part_o = p.part_o;
     mp.part_ml = p.part_ml;

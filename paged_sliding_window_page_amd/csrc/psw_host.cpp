@@ -257,71 +257,94 @@ int32_t effective_decode_mode(const PlanState& st, int32_t mode) {
 void build_decode_schedule(const PlanState& st, int64_t wl, int32_t mode, DecodeSchedule* out) {
   // keys each request must read: the window (or everything) ending at p = kv_len - 1
   std::vector<int64_t> lo(st.batch), n(st.batch);
-  int64_t key_heads = 0;
+  int64_t n_max = 0;
   for (int32_t b = 0; b < st.batch; ++b) {
     const int64_t p = int64_t(st.kv_len[b]) - 1;
     lo[b] = wl >= 0 ? std::max<int64_t>(0, p - wl) : 0;
     n[b] = p - lo[b] + 1;
-    key_heads += n[b] * st.num_kv_heads;
+    n_max = std::max(n_max, n[b]);
   }
-  // One work-group per (split, KV head), about kDecodeTargetUnits of them
-  // (2 to 4 waves each: two rounds of the 256 CUs at 8 waves per CU).  A split
-  // writes group x head_dim fp32 partials that the merge reads back, against
-  // 4 x head_dim bytes of K and V per key: at least 16 x group keys per split
-  // keeps that traffic under 1/16 of the K/V stream.
-  const int64_t unit = kDecodeSplitUnit;
-  int64_t chunk = (key_heads + kDecodeTargetUnits - 1) / kDecodeTargetUnits;
-  chunk = std::max<int64_t>(chunk, 16 * int64_t(st.group));
-  chunk = std::max<int64_t>(unit, (chunk + unit - 1) / unit * unit);
-  // Non-partitioned form: one work-group per (request, KV head) reads all of
-  // the request's keys and writes O itself (no partials, no merge launch).
-  int64_t n_max = 0;
-  for (int32_t b = 0; b < st.batch; ++b) n_max = std::max(n_max, n[b]);
+  // The decode kernel runs a list of items per work-group and writes whole
+  // requests itself; the attention kernel (wider groups) runs one item per
+  // work-group and always writes partials.
+  const bool decode_kernel = st.group <= kDecodeKernelMaxGroup;
+  // Direct form: one work-group per (request, KV head) reads all of the
+  // request's keys and writes O (no partials, no merge launch).
   const bool full_grid = int64_t(st.batch) * st.num_kv_heads >= kDecodeFullGrid;
   const int64_t direct_keys = full_grid ? kDecodeDirectKeysFull
                               : st.head_dim == 256 ? kDecodeDirectKeys256
                                                    : kDecodeDirectKeys512;
-  const bool direct = mode == PSW_DECODE_DIRECT ||
-                      (mode == PSW_DECODE_AUTO && n_max <= direct_keys);
-  if (direct) chunk = std::max<int64_t>(chunk, (n_max + unit - 1) / unit * unit);
-  // Each request's keys are cut into ceil(n / chunk) nearly equal splits at
-  // multiples of kDecodeSplitUnit (absolute key index, so no KV tile is read
-  // by two splits).  Items are then ordered longest first, so the short
-  // splits fill in behind the long ones at the end of the launch.
-  struct Split { int32_t b, slot, lo, hi; };
-  std::vector<Split> splits;
+  const bool direct = decode_kernel && (mode == PSW_DECODE_DIRECT ||
+                                        (mode == PSW_DECODE_AUTO && n_max <= direct_keys));
+  out->items.clear();
+  out->wg_items.clear();
   out->req_splits.assign(2 * st.batch, 0);
   int32_t slot = 0;
-  for (int32_t b = 0; b < st.batch; ++b) {
-    const int32_t first = slot;
-    const int64_t end = lo[b] + n[b];
-    const int64_t ns = (n[b] + chunk - 1) / chunk;
-    int64_t k0 = lo[b];
-    for (int64_t i = 1; i <= ns; ++i) {
-      int64_t k1 = end;
-      if (i < ns) {
-        k1 = (lo[b] + i * n[b] / ns + unit / 2) / unit * unit;
-        if (k1 <= k0 || k1 >= end) continue;
-      }
-      splits.push_back({b, slot++, int32_t(k0), int32_t(k1 - 1)});
-      k0 = k1;
+  if (direct) {
+    // longest first, so the short requests fill in behind the long ones
+    std::vector<int32_t> order(st.batch);
+    for (int32_t b = 0; b < st.batch; ++b) order[b] = b;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t x, int32_t y) { return n[x] > n[y]; });
+    for (int32_t b : order) {
+      out->wg_items.push_back(static_cast<int32_t>(out->items.size() / 4));
+      out->items.insert(out->items.end(), {b, -1, int32_t(lo[b]), int32_t(lo[b] + n[b] - 1)});
     }
-    out->req_splits[2 * b] = first;
-    out->req_splits[2 * b + 1] = slot - first;
+  } else {
+    // Split form.  The requests' keys, in units of kDecodeSplitUnit keys at
+    // absolute multiples (so no decode tile is read by two pieces), are laid
+    // end to end in request order and cut into equal contiguous shares, one
+    // per work-group, at most as many work-groups as are resident at once:
+    // every work-group streams the same amount and the launch ends together.
+    // A share covers pieces of one or more requests; a piece that is a whole
+    // request is written directly, the others get a partial slot each, and
+    // the pieces of a request are consecutive, so its slots are too.
+    const int64_t unit = kDecodeSplitUnit;
+    std::vector<int64_t> u0(st.batch), start(st.batch + 1, 0);
+    for (int32_t b = 0; b < st.batch; ++b) {
+      u0[b] = lo[b] / unit;
+      start[b + 1] = start[b] + (lo[b] + n[b] - 1) / unit - u0[b] + 1;
+    }
+    const int64_t total = start[st.batch];
+    // A piece writes group x head_dim fp32 partials that the merge reads back,
+    // against 4 x head_dim bytes of K and V per key: shares of at least
+    // 16 x group keys keep that traffic under 1/16 of the K/V stream.
+    const int64_t min_units = std::max<int64_t>(1, (16 * int64_t(st.group) + unit - 1) / unit);
+    const int64_t waves = st.head_dim / 128;
+    const int64_t resident =
+        std::max<int64_t>(1, kDecodeResidentWaves / waves / st.num_kv_heads);
+    const int64_t groups =
+        std::min(resident, std::max<int64_t>(1, (total + min_units - 1) / min_units));
+    int32_t b = 0;
+    for (int64_t g = 0; g < groups; ++g) {
+      int64_t s0 = total * g / groups;
+      const int64_t s1 = total * (g + 1) / groups;
+      out->wg_items.push_back(static_cast<int32_t>(out->items.size() / 4));
+      while (s0 < s1) {
+        while (start[b + 1] <= s0) ++b;
+        const int64_t a = s0 - start[b];
+        const int64_t e = std::min(s1, start[b + 1]) - start[b];
+        const int64_t k0 = std::max(lo[b], (u0[b] + a) * unit);
+        const int64_t k1 = std::min(lo[b] + n[b] - 1, (u0[b] + e) * unit - 1);
+        const bool whole = a == 0 && start[b] + e == start[b + 1];
+        int32_t sl = -1;
+        if (!(whole && decode_kernel)) {
+          if (out->req_splits[2 * b + 1] == 0) out->req_splits[2 * b] = slot;
+          ++out->req_splits[2 * b + 1];
+          sl = slot++;
+        }
+        out->items.insert(out->items.end(), {b, sl, int32_t(k0), int32_t(k1)});
+        s0 = start[b] + e;
+      }
+    }
   }
-  std::stable_sort(splits.begin(), splits.end(), [](const Split& x, const Split& y) {
-    return x.hi - x.lo > y.hi - y.lo;
-  });
-  out->items.clear();
-  out->items.reserve(4 * splits.size());
-  for (const Split& sp : splits) out->items.insert(out->items.end(), {sp.b, sp.slot, sp.lo, sp.hi});
+  out->wg_items.push_back(static_cast<int32_t>(out->items.size() / 4));
   out->num_partials = slot;
+  out->num_wgs = decode_kernel ? static_cast<int32_t>(out->wg_items.size() - 1)
+                               : static_cast<int32_t>(out->items.size() / 4);
   out->window_left = wl;
   out->mode = mode;
-  out->chunk = static_cast<int32_t>(chunk);
-  // the direct form only when it was chosen (a split schedule keeps its
-  // partials and merge even where every request fits one split)
-  out->direct = direct && slot == st.batch;
+  out->direct = slot == 0;
 }
 
 void build_prep_items(const PlanState& st, std::vector<int32_t>* out) {
@@ -505,7 +528,7 @@ int psw_plan_decode_form(const psw_plan* plan, int64_t window_left, int32_t* dir
   psw::build_decode_schedule(st, psw::effective_window(st, window_left),
                              psw::effective_decode_mode(st, plan->decode_mode), &ds);
   *direct = ds.direct ? 1 : 0;
-  *work_groups = int64_t(ds.num_partials) * st.num_kv_heads;
+  *work_groups = int64_t(ds.num_wgs) * st.num_kv_heads;
   return PSW_OK;
 }
 

@@ -42,9 +42,8 @@ constexpr int kPrefillRows = 256;          // query rows (token x head) per work
 constexpr int kPrefillRows512 = 64;        // the same at head_dim 512 (dims split over wave pairs)
 constexpr int kKvTile256 = 64;             // keys per prefill tile at head_dim 256
 constexpr int kKvTile512 = 32;             // keys per prefill tile at head_dim 512
-constexpr int kDecodeTile = 16;            // keys per decode MFMA step (one wave per split)
-constexpr int kDecodeSplitUnit = 64;       // split boundaries are multiples of this key index
-constexpr int kDecodeTargetUnits = 2048;   // decode (split, KV head) work-groups aimed for
+constexpr int kDecodeSplitUnit = 64;       // decode pieces start and end at multiples of this key index
+constexpr int kDecodeResidentWaves = 2048; // decode kernel waves resident at once (256 CUs x 8)
 // Automatic decode form (measured on MI355X, split vs direct over batch x KV
 // length): the direct form wins while its longest work-group loop stays
 // shorter than the split form's extra merge launch -- up to about 160 keys at
@@ -103,11 +102,14 @@ void build_prefill_schedule(const PlanState& st, int64_t window_left, int32_t kv
 struct DecodeSchedule {
   int64_t window_left = -2;
   int32_t mode = -1;                 // PSW_DECODE_* the schedule was built for
-  int32_t chunk = 0;                 // keys per split
-  bool direct = false;               // one split per request: O written by the decode kernel
-  std::vector<int32_t> items;        // quads
-  std::vector<int32_t> req_splits;   // pairs (first partial slot, number of splits) per request
+  bool direct = false;               // every item a whole request: no partials, no merge launch
+  // quads (request, partial slot or -1 for a whole request written by the
+  // decode kernel, first key, last key)
+  std::vector<int32_t> items;
+  std::vector<int32_t> wg_items;     // decode kernel: work-group g runs items [wg_items[g], wg_items[g+1])
+  std::vector<int32_t> req_splits;   // pairs (first partial slot, number of pieces) per request
   int32_t num_partials = 0;
+  int32_t num_wgs = 0;               // work-groups per KV head of the decode launch
 };
 void build_decode_schedule(const PlanState& st, int64_t window_left, int32_t mode,
                            DecodeSchedule* out);
