@@ -95,7 +95,6 @@ struct PrepParams {
   __bf16* pool;
   int32_t* err;
   const int32_t* items;
-  const int32_t* wg_items;  // decode kernel: items of work-group g are [wg_items[g], wg_items[g+1])
   PoolStrides ps;
   int64_t layer_off;
   int32_t num_qo_heads;

@@ -418,7 +418,13 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   // of K(u-1), which both groups finished reading in the slot before, while
   // it waits at the barrier for group 1's softmax.
   auto mfma_phase = [&](int u, auto pv_c, auto qk_c) __attribute__((always_inline)) {
+    // the wave in its MFMA phase takes issue priority over the softmax wave
+    // on the same SIMD, so the matrix unit is not left waiting on VALU issue
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
     mfma_seq(pv_c, qk_c, vbuf(u + 2), kbuf(u));
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
     if (decltype(qk_c)::value && grp == 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) k_load(kbuf(u + 2), (jt0 + u + 2) * KT, tpid, r);
