@@ -3,7 +3,9 @@ oracle, through the C ABI.
 
 Decode is the prefill entry called with one query per request (PR
 "feat(gemma4): paged KV serving across both attention families", Description).
-The library runs it as split-KV partials plus a merge; these cases cover the
+The library runs it either as one work-group per request or as equal shares
+of the batch's keys (pieces of cut requests write partials that a merge
+combines); these cases cover the
 page-size modes of the decode kernel (pages of 8, 16 and >= 32 slots), the GQA
 group widths (up to 16 query heads per KV head in the decode kernel, 32 through
 the general split kernel), windows that start mid-tile, NaN outside the keys
@@ -157,3 +159,20 @@ def test_decode_forms_agree_on_short_requests(hd):
     ref = oracle_attention(case, window_left=wl)
     check_close(direct, ref, "direct")
     check_close(split, ref, "split")
+
+
+@pytest.mark.parametrize("hd", [256, 512])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_decode_shares_span_requests(hd, out_dtype):
+    """Split form on a batch whose equal shares cross request boundaries: 150
+    short requests (1..200 keys) around three long ones, so work-groups run
+    several whole requests in a row (each writing O itself) next to pieces of
+    the long requests (partials, merged afterwards); the exchange-buffer parity
+    carries over between the items of a work-group."""
+    g = np.random.default_rng(5)
+    kv = [int(x) for x in g.integers(1, 201, 150)]
+    kv[10], kv[75], kv[140] = 3000, 9000, 5000
+    case = _case(hd, 79, kv, num_pages=sum((k + 15) // 16 for k in kv) + 8)
+    wl = 700 if hd == 256 else -1
+    gpu = _run_decode_entry(case, 1, wl, out_dtype)
+    check_close(gpu, oracle_attention(case, window_left=wl), f"decode shares hd{hd}")
