@@ -616,46 +616,40 @@ __global__ __launch_bounds__(D / 4) void merge_kernel(MergeParams P) {
   const int first = P.req_splits[2 * b];
   const int ns = P.req_splits[2 * b + 1];
   if (ns == 0) return;  // the decode kernel wrote this request's O itself
-  // Splits are combined 8 at a time with all their loads issued first, so the
-  // loop runs at memory throughput rather than one load latency per split.
-  constexpr int U = 8;
+  // One pass with a running maximum: 16 splits at a time, all of their loads
+  // issued first, so a request with up to 16 splits costs one memory round
+  // trip after its split list.
+  constexpr int U = 16;
   const float* ml = P.part_ml + ((int64_t)first * P.num_qo_heads + head) * 2;
   const int64_t ml_stride = 2 * (int64_t)P.num_qo_heads;
-  float M = kNegBig;
-  int s = 0;
-  for (; s + U <= ns; s += U) {
-    float m[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) m[u] = ml[(s + u) * ml_stride];
-#pragma unroll
-    for (int u = 0; u < U; ++u) M = fmaxf(M, m[u]);
-  }
-  for (; s < ns; ++s) M = fmaxf(M, ml[s * ml_stride]);
-  float L = 0.0f;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   const int d = 4 * threadIdx.x;
   const float* po = P.part_o + ((int64_t)first * P.num_qo_heads + head) * D + d;
   const int64_t po_stride = (int64_t)P.num_qo_heads * D;
-  for (s = 0; s + U <= ns; s += U) {
+  float M = kNegBig, L = 0.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = 0; s0 < ns; s0 += U) {
     float m[U], l[U];
     f32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      m[u] = ml[(s + u) * ml_stride];
-      l[u] = ml[(s + u) * ml_stride + 1];
-      v[u] = *reinterpret_cast<const f32x4*>(po + (s + u) * po_stride);
+      const int sp = min(s0 + u, ns - 1);  // past the end: repeat the last split (weight 0 below)
+      m[u] = ml[sp * ml_stride];
+      l[u] = ml[sp * ml_stride + 1];
+      v[u] = *reinterpret_cast<const f32x4*>(po + sp * po_stride);
     }
+    float mx = M;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx = s0 + u < ns ? fmaxf(mx, m[u]) : mx;
+    const float r = __builtin_amdgcn_exp2f(M - mx);  // rescale what is summed so far
+    L *= r;
+    acc *= r;
+    M = mx;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float wgt = __builtin_amdgcn_exp2f(m[u] - M);
+      const float wgt = s0 + u < ns ? __builtin_amdgcn_exp2f(m[u] - M) : 0.0f;
       L += wgt * l[u];
       acc += wgt * v[u];
     }
-  }
-  for (; s < ns; ++s) {
-    const float wgt = __builtin_amdgcn_exp2f(ml[s * ml_stride] - M);
-    L += wgt * ml[s * ml_stride + 1];
-    acc += wgt * *reinterpret_cast<const f32x4*>(po + s * po_stride);
   }
   const float inv = 1.0f / L;
   const int64_t orow = ((int64_t)P.qo_indptr[b] * P.num_qo_heads + head) * D + d;
