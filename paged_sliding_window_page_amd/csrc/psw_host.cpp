@@ -313,8 +313,11 @@ void build_decode_schedule(const PlanState& st, int64_t wl, int32_t mode, Decode
     const int64_t waves = st.head_dim / 128;
     const int64_t resident =
         std::max<int64_t>(1, kDecodeResidentWaves / waves / st.num_kv_heads);
-    const int64_t groups =
-        std::min(resident, std::max<int64_t>(1, (total + min_units - 1) / min_units));
+    // at least one work-group per request (up to the resident count): a
+    // work-group runs its items one after another, each paying the latency of
+    // its first loads, so short requests are not stacked several deep
+    const int64_t groups = std::min(
+        resident, std::max<int64_t>({1, (total + min_units - 1) / min_units, int64_t(st.batch)}));
     int32_t b = 0;
     for (int64_t g = 0; g < groups; ++g) {
       int64_t s0 = total * g / groups;
