@@ -202,7 +202,7 @@ int psw_prefill_tile_q(int64_t group, int64_t head_dim, int32_t* tile_q);
  *                unscaled attention the model runs)
  *   window_left: key j is visible to the query at position p iff
  *                0 <= p - j <= window_left (inclusive distance); -1 = no window
- * qo_len == 1 for every request selects the split-KV decode kernels, otherwise
+ * qo_len == 1 for every request selects the decode kernels, otherwise
  * the MFMA prefill kernel runs ([P3] Description: the serving loop's decode
  * step is a call of this entry with one query token per request). */
 int paged_prefill_window_hd256(psw_plan* plan, const psw_pool* pool, int64_t layer,
@@ -224,9 +224,13 @@ int paged_prefill_hd512(psw_plan* plan, const psw_pool* pool, int64_t layer,
  * every request (PSW_E_SHAPE otherwise) and are otherwise identical to
  * paged_prefill_window_hd256 / paged_prefill_hd512.
  * Two forms, chosen per call by the plan's decode mode:
- *   PSW_DECODE_SPLIT   each request's keys cut into splits (about 2048
- *                      (split, KV head) work-groups per launch), fp32 partial
- *                      results in the plan's workspace, then a merge launch;
+ *   PSW_DECODE_SPLIT   the batch's keys (64-key units) laid end to end and
+ *                      cut into equal shares, one per work-group (as many as
+ *                      are resident at once, at least one per request, at
+ *                      most one per unit); a request inside one share is
+ *                      written directly, the pieces of a request cut between
+ *                      shares write fp32 partials to the plan's workspace and
+ *                      a merge launch combines them;
  *   PSW_DECODE_DIRECT  one work-group per (request, KV head) over all of its
  *                      keys, writing O itself: no workspace, no merge;
  *   PSW_DECODE_AUTO    DIRECT while every request reads at most 160 keys
@@ -237,9 +241,11 @@ int paged_prefill_hd512(psw_plan* plan, const psw_pool* pool, int64_t layer,
  * A GQA group of 32 always takes SPLIT. */
 enum { PSW_DECODE_AUTO = 0, PSW_DECODE_SPLIT = 1, PSW_DECODE_DIRECT = 2 };
 int psw_plan_set_decode_mode(psw_plan* plan, int32_t mode);
-/* What the next decode call with this window would launch: *direct = 1 for
- * the direct form, *work_groups = (split, KV head) work-groups of the decode
- * launch.  PSW_E_SHAPE when the plan has a request with qo_len > 1. */
+/* What the next decode call with this window would launch: *direct = 1 when
+ * it writes no partials (the direct form, or a split in which no request is
+ * cut) and so has no merge launch, *work_groups = the decode launch's
+ * work-groups (shares or requests, times KV heads).  PSW_E_SHAPE when the
+ * plan has a request with qo_len > 1. */
 int psw_plan_decode_form(const psw_plan* plan, int64_t window_left, int32_t* direct,
                          int64_t* work_groups);
 int paged_decode_window_hd256(psw_plan* plan, const psw_pool* pool, int64_t layer,
