@@ -91,6 +91,16 @@ const char* psw_last_error(void);
 /* Library version as a static string. */
 const char* psw_version(void);
 
+/* Diagnostic, off the hot path: the shader clock in MHz while every CU issues
+ * bf16 MFMAs (eight waves per CU of back-to-back v_mfma_f32_32x32x16_bf16, the
+ * prefill kernels' occupancy), from the shader-clock and constant-rate
+ * counters of each work-group.  The MFMA peak scales with this clock, so a
+ * benchmark can report its fraction of the clock-adjusted peak next to the
+ * nominal one.  Runs two short launches on `stream` (~1 ms each), allocates
+ * and frees a small device buffer, and waits for the stream.  PSW_E_NULL for
+ * a NULL `mhz`, PSW_E_HIP when the device or a launch fails. */
+int psw_measure_mfma_clock(psw_stream_t stream, double* mhz);
+
 /* ---------------------------------------------------------------- pool ---- */
 
 /* A caller-owned bf16 pool in the layout above.  Geometry is re-derived with

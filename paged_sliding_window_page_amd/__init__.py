@@ -100,6 +100,7 @@ def _sig(name, res, *args):
 
 _last_error = _sig("psw_last_error", ctypes.c_char_p)
 _version = _sig("psw_version", ctypes.c_char_p)
+_mfma_clock = _sig("psw_measure_mfma_clock", ctypes.c_int, c_vp, ctypes.POINTER(ctypes.c_double))
 _check_pool = _sig("psw_check_pool", ctypes.c_int, ctypes.POINTER(PoolDesc))
 _plan_create = _sig("psw_plan_create", ctypes.c_int, ctypes.POINTER(PlanDesc), c_vp,
                     ctypes.POINTER(c_vp))
@@ -150,12 +151,20 @@ EXPORTS = ["psw_last_error", "psw_version", "psw_check_pool", "psw_plan_create",
            "q_norm_rope_prefill_hd512", "psw_rope_tables", "psw_plan_device_errors",
            "psw_kv_server_create", "psw_kv_server_destroy", "psw_kv_server_free_pages",
            "psw_kv_request_create", "psw_kv_request_release", "psw_kv_request_info",
-           "psw_kv_admit", "psw_kv_commit", "psw_kv_abort", "psw_kv_step_tables"]
+           "psw_kv_admit", "psw_kv_commit", "psw_kv_abort", "psw_kv_step_tables",
+           "psw_measure_mfma_clock"]
 
 
 def _check(rc: int):
     if rc != PSW_OK:
         raise PswError(rc, _last_error().decode(errors="replace"))
+
+
+def measure_mfma_clock(stream=None) -> float:
+    """Shader clock (MHz) with every CU issuing bf16 MFMAs (diagnostic)."""
+    mhz = ctypes.c_double()
+    _check(_mfma_clock(_stream_handle(stream), ctypes.byref(mhz)))
+    return mhz.value
 
 
 def version() -> str:

@@ -425,3 +425,8 @@ def test_ring_attention_needs_the_window_inside_the_ring():
 def test_ring_prep_refuses_a_step_longer_than_its_ring():
     plan = _ring_plan([100, 16], qo=(40, 4))  # 40 positions into 32 slots
     assert _code(lambda: _prep(plan, _pool(), positions=128)) == "PSW_E_RANGE"
+
+
+def test_mfma_clock_probe_rejects_null():
+    # checked before any device call, so it runs without a GPU
+    assert _code(lambda: psw._check(psw._mfma_clock(None, None))) == "PSW_E_NULL"
