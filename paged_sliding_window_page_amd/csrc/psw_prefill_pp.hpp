@@ -93,15 +93,6 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   // registers): [wave][k-step 8..15][lane] chunks of 16 bytes
   constexpr int KSR = KS / 2;     // QK k-steps whose Q operand is in registers
   __shared__ __attribute__((aligned(1024))) char qlds[NW * (KS - KSR) * 1024];
-  auto kbuf = [&](int i) __attribute__((always_inline)) -> char* {
-    i %= 3;
-    return i == 0 ? kb0 : (i == 1 ? kb1 : kb2);
-  };
-  auto vbuf = [&](int i) __attribute__((always_inline)) -> char* {
-    i %= 3;
-    return i == 0 ? vb0 : (i == 1 ? vb1 : vb2);
-  };
-
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = w >> 2;   // 0: MFMA first, 1: ALU first
@@ -385,6 +376,17 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
     lds_barrier();
   }
 
+  // The three K and three V tile buffers by role, rotated at the end of every
+  // MFMA phase so that no phase computes a buffer index: during MFMA(u), K0,
+  // K1, K2 hold K(u), K(u+1), K(u+2) and V0, V1, V2 hold V(u-1), V(u),
+  // V(u+1); during ALU(j), which follows MFMA(j), K0 holds K(j+1) and V0, V1,
+  // V2 hold V(j), V(j+1), V(j+2).
+  char* K0 = kb0;
+  char* K1 = kb1;
+  char* K2 = kb2;
+  char* V0 = vb2;
+  char* V1 = vb0;
+  char* V2 = vb1;
   // ALU(j): this group's loads, softmax of S(j) (if j is a tile), barrier.
   auto alu_phase = [&](int j) __attribute__((always_inline)) {
     int64_t tn[2] = {0, 0};
@@ -395,22 +397,22 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
         int64_t p0[2] = {0, 0};
         fetch_pids(0, p0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v_load(vbuf(0), jt0 * KT, p0, r);
+        for (int r = 0; r < 4; ++r) v_load(V1, jt0 * KT, p0, r);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v_load(vbuf(j + 2), (jt0 + j + 2) * KT, tpid, r);
+      for (int r = 0; r < 4; ++r) v_load(V2, (jt0 + j + 2) * KT, tpid, r);
     }
     if (j >= 0 && j < ntiles) softmax((jt0 + j) * KT);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(4 | 0x70 | 0xF00);  // vmcnt(4): the loads before the last landed
     asm volatile("" ::: "memory");
-    if (grp == 1) v_tile_sanitize(vbuf(j + 1), (jt0 + j + 1) * KT);
+    if (grp == 1) v_tile_sanitize(V1, (jt0 + j + 1) * KT);
 #pragma unroll
     for (int p = 0; p < 2; ++p) tpid[p] = tn[p];
     // first operands of MFMA(j+1): V(j) (resident since the end of slot
     // 2j), or K(0) before the first phase
-    if (j >= 0) preload(std::true_type{}, vbuf(j), kbuf(j + 1));
-    else preload(std::false_type{}, vbuf(0), kbuf(0));
+    if (j >= 0) preload(std::true_type{}, V0, K0);
+    else preload(std::false_type{}, V1, K0);
     lds_barrier();
   };
   // MFMA(u): PV(u-1) from V(u-1) (if u >= 1), QK(u) from K(u) (if u <
@@ -422,21 +424,30 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
     // on the same SIMD, so the matrix unit is not left waiting on VALU issue
     __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_seq(pv_c, qk_c, vbuf(u + 2), kbuf(u));
+    mfma_seq(pv_c, qk_c, V0, K0);
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     if (decltype(qk_c)::value && grp == 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) k_load(kbuf(u + 2), (jt0 + u + 2) * KT, tpid, r);
+      for (int r = 0; r < 4; ++r) k_load(K2, (jt0 + u + 2) * KT, tpid, r);
     }
     lds_barrier();
+    // the next tile's view of the rings
+    char* const kt = K0;
+    K0 = K1;
+    K1 = K2;
+    K2 = kt;
+    char* const vt = V0;
+    V0 = V1;
+    V1 = V2;
+    V2 = vt;
   };
 
   fetch_pids(grp == 0 ? 2 : 1, tpid);
   // group 1 starts with ALU(-1) (no softmax, the first V loads); group 0
   // with MFMA(0)
   // the first MFMA phase (QK only) and the last (PV only) are peeled off
-  if (grp == 0) preload(std::false_type{}, vbuf(0), kbuf(0));
+  if (grp == 0) preload(std::false_type{}, V1, K0);
   else alu_phase(-1);
   mfma_phase(0, std::false_type{}, std::true_type{});
   for (int u = 1; u < ntiles; ++u) {
