@@ -264,13 +264,15 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
     const bool need = __any(m_new > m_run + kSlack);
     const float m_use = need ? m_new : m_run;
     const float cmul = full ? c2 : 1.0f;
-    float lsum = 0.0f;
+    // four partial row sums: a short dependency chain
+    float ls[4];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], cmul, -m_use));
-      lsum += p;
+      ls[r & 3] = r < 4 ? p : ls[r & 3] + p;
       pb[r >> 3][r & 7] = (__bf16)p;
     }
+    const float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
     if (need) {
       rare_path();
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -280,9 +282,10 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
       for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
     }
     l_run += lsum;
-    // P(t) complete here, inside the ALU phase: keep the compiler from
-    // sinking the exponentials into the next MFMA phase
-    asm volatile("" ::"v"(pb[0]), "v"(pb[1]));
+    // P(t) and the row sum complete here, inside the ALU phase: keep the
+    // compiler from sinking the exponentials or the additions into the next
+    // MFMA phase
+    asm volatile("" : "+v"(l_run) : "v"(pb[0]), "v"(pb[1]));
   };
 
   // Tile loads: group 0 loads K(u+2) at the end of its MFMA(u), group 1
