@@ -104,7 +104,8 @@ int psw_measure_mfma_clock(psw_stream_t stream, double* mhz);
 /* ---------------------------------------------------------------- pool ---- */
 
 /* A caller-owned bf16 pool in the layout above.  Geometry is re-derived with
- * overflow-checked multiplies and must match numel exactly (whole pages). */
+ * overflow-checked multiplies and must match numel exactly (whole pages); a
+ * page (its K and V blocks) must stay under 4 GiB (PSW_E_UNSUPPORTED). */
 typedef struct {
   void* base;            /* device, bf16, numel elements                        */
   int64_t numel;

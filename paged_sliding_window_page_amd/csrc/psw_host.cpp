@@ -16,6 +16,8 @@
 //        that positions stay inside the RoPE tables, and the table sizes.
 #include "psw_host.hpp"
 
+#include <cstdint>
+
 #include <algorithm>
 #include <cmath>
 #include <cstring>
@@ -74,6 +76,10 @@ int check_pool(const psw_pool* p, bool need_base) {
     return fail(PSW_E_SHAPE, "pool numel " + std::to_string(p->numel) +
                                  " != layers*pages*2*kv_heads*page_size*head_dim = " +
                                  std::to_string(n));
+  // the kernels form a page's byte offset as a 32-bit page id times a 32-bit
+  // page size
+  if (2 * p->num_kv_heads * p->page_size * p->head_dim * 2 > int64_t(UINT32_MAX))
+    return fail(PSW_E_UNSUPPORTED, "a pool page (K and V blocks) is 4 GiB or more");
   return PSW_OK;
 }
 

@@ -230,9 +230,12 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
 
   // Softmax of S(t) (tile starting at key j0) into P(t); rescales O if the
   // running max rose past the slack.
+  // Tiles inside every row's keys and window (no element mask): tile starts
+  // j0 in [full_lo, full_hi], worked out once.
+  const int full_lo = wave_live ? max(k_lo, wl >= 0 ? w_pmax - wl : k_lo) : 0x7fffffff;
+  const int full_hi = min(k_hi, w_pmin) - (KT - 1);
   auto softmax = [&](int j0) __attribute__((always_inline)) {
-    const bool full = wave_live && j0 >= k_lo && j0 + KT - 1 <= k_hi && j0 + KT - 1 <= w_pmin &&
-                      (wl < 0 || w_pmax - j0 <= wl);
+    const bool full = j0 >= full_lo && j0 <= full_hi;
     float mx = -__builtin_inff();
     if (full) {
       // max of s * c2: c2 times the max of s, or of the min for a negative c2
@@ -294,11 +297,38 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   // loads, and group 1 zeroes the keys past kv_len of V(j+1).  With 16-slot
   // pages the page ids of a tile are read through the scalar cache in the ALU
   // phase before its loads.
-  int64_t tpid[2] = {0, 0};  // page ids of this wave's next tile
+  // 16-slot pages: a tile is two pages; tp holds their byte offsets in the
+  // pool (page id x page bytes, from 32-bit halves: a page of this geometry
+  // is far below 4 GiB).
+  const uint32_t pb32 = (uint32_t)page_bytes;
+  int64_t tpid[2] = {0, 0};  // page byte offsets of this wave's next tile
   auto fetch_pids = [&](int tile, int64_t* tp) __attribute__((always_inline)) {
     if constexpr (PAGE16) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p) tp[p] = page_id(((jt0 + tile) * KT >> 4) + p);
+      for (int p = 0; p < 2; ++p)
+        tp[p] = (int64_t)((uint64_t)(uint32_t)page_id(((jt0 + tile) * KT >> 4) + p) * pb32);
+    }
+  };
+  // The loop's fetches walk the page list one tile (two entries) at a time
+  // as a byte offset modulo the list length, instead of clamping and mapping
+  // every index: tiles past the last page then read other pages of the
+  // request, whose keys are masked and whose V is zeroed like any key past
+  // kv_len.  pl4: byte offset of the next fetched tile's first entry.
+  const int n_list = last_page + 1;
+  const uint32_t n4 = 4u * (uint32_t)n_list;
+  uint32_t pl4 = 4u * (uint32_t)((2 * (jt0 + (grp == 0 ? 3 : 2))) % n_list);
+  auto list_at = [&](uint32_t off) __attribute__((always_inline)) {
+    return ldu(reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(pages) + off));
+  };
+  auto fetch_next = [&](int64_t* tp) __attribute__((always_inline)) {
+    if constexpr (PAGE16) {
+      uint32_t p1 = pl4 + 4u;
+      if (p1 >= n4) p1 -= n4;
+      tp[0] = (int64_t)((uint64_t)(uint32_t)list_at(pl4) * pb32);
+      tp[1] = (int64_t)((uint64_t)(uint32_t)list_at(p1) * pb32);
+      pl4 += 8u;
+      if (pl4 >= n4) pl4 -= n4;
+      if (pl4 >= n4) pl4 -= n4;
     }
   };
   // One load instruction r (0..3) of wave wg of the loading group: K rows
@@ -309,7 +339,7 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
       // key 8 r + 2 wg + h of the tile (page r / 2), chunk n ^ kswz(key)
       const int key = 8 * (r & 1) + 2 * wg + h;
       const uint32_t off = key * D * 2 + ((n ^ kswz(key)) << 4);
-      lds_dma16_s(kbase_g + kp[r >> 1] * page_bytes, off, kl + (4 * r + wg) * 1024);
+      lds_dma16_s(kbase_g + kp[r >> 1], off, kl + (4 * r + wg) * 1024);
     } else {
       const int ins = 4 * r + wg;
       const int u = ins * 64 + lane;
@@ -324,7 +354,7 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   auto v_load = [&](char* vl, int jj, const int64_t* vp, int r) __attribute__((always_inline)) {
     if constexpr (PAGE16) {
       // keys 8 r .. 8 r + 7 of the tile (page r / 2), dim 64 wg + lane
-      lds_dma16_s(vbase_g + vp[r >> 1] * page_bytes + 16 * (r & 1), (64 * wg + lane) * 32,
+      lds_dma16_s(vbase_g + vp[r >> 1] + 16 * (r & 1), (64 * wg + lane) * 32,
                   vl + (4 * r + wg) * 1024);
     } else {
       const int ins = 4 * r + wg;
@@ -393,7 +423,7 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   // ALU(j): this group's loads, softmax of S(j) (if j is a tile), barrier.
   auto alu_phase = [&](int j) __attribute__((always_inline)) {
     int64_t tn[2] = {0, 0};
-    fetch_pids(j + 3, tn);
+    fetch_next(tn);   // tile j + 3
     if (grp == 1) {
       if (j < 0) {
         rare_path();

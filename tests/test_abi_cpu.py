@@ -168,6 +168,10 @@ def test_pool_checks():
     big = psw.pool_desc(FAKE, numel=1, num_layers=2 ** 30, num_pages=2 ** 30, page_size=16,
                         num_kv_heads=8, head_dim=256)
     assert _code(lambda: psw.check_pool(big)) == "PSW_E_OVERFLOW"
+    # a page of 4 GiB or more: 2 (K, V) x 4096 heads x 1024 slots x 256 dims x 2 B
+    huge = _pool(num_layers=1, num_pages=1, num_kv_heads=4096, page_size=1024)
+    assert _code(lambda: psw.check_pool(huge)) == "PSW_E_UNSUPPORTED"
+    psw.check_pool(_pool(num_layers=1, num_pages=1, num_kv_heads=2047, page_size=1024))
 
 
 # ------------------------------------------------------------- attention ----
