@@ -300,8 +300,9 @@ void build_decode_schedule(const PlanState& st, int64_t wl, int32_t mode, Decode
     // Split form.  The requests' keys, in units of kDecodeSplitUnit keys at
     // absolute multiples (so no decode tile is read by two pieces), are laid
     // end to end in request order and cut into equal contiguous shares, one
-    // per work-group, at most as many work-groups as are resident at once:
-    // every work-group streams the same amount and the launch ends together.
+    // per work-group, at most kDecodeResidentWaves' worth of work-groups (all
+    // of them run at once): every work-group streams the same amount and the
+    // launch ends together.
     // A share covers pieces of one or more requests; a piece that is a whole
     // request is written directly, the others get a partial slot each, and
     // the pieces of a request are consecutive, so its slots are too.

@@ -43,7 +43,10 @@ constexpr int kPrefillRows512 = 64;        // the same at head_dim 512 (dims spl
 constexpr int kKvTile256 = 64;             // keys per prefill tile at head_dim 256
 constexpr int kKvTile512 = 32;             // keys per prefill tile at head_dim 512
 constexpr int kDecodeSplitUnit = 64;       // decode pieces start and end at multiples of this key index
-constexpr int kDecodeResidentWaves = 2048; // decode kernel waves resident at once (256 CUs x 8)
+// Waves the split decode spreads over the GPU: four per CU (256 CUs).  The
+// kernel could keep eight per CU resident, but the equal-share launch streams
+// K/V faster with four (measured: global-family batch 116 -> 104 us).
+constexpr int kDecodeResidentWaves = 1024;
 // Automatic decode form (measured on MI355X, split vs direct over batch x KV
 // length): the direct form wins while its longest work-group loop stays
 // shorter than the split form's extra merge launch -- up to about 160 keys at
