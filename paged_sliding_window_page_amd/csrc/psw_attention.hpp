@@ -54,6 +54,30 @@ __device__ __forceinline__ int kswz(int key) {
   return (key & 3) | ((key >> 1) & 4) | ((key << 1) & 8);
 }
 
+// global_load_lds_dwordx4 issued as inline assembly: 16 bytes per lane from
+// gsrc into LDS at lds_base + 16 * lane.  The compiler does not track these
+// loads: a kernel that uses them orders them itself, with explicit vmcnt
+// waits and barriers, against the LDS reads of the buffers they fill (the
+// compiler would otherwise wait for every load in flight before unrelated
+// LDS reads, and rebuild a 64-bit vector address for every load).
+__device__ __forceinline__ void lds_dma16(const void* gsrc, const char* lds_dst) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_dst;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(m0)
+               : "memory", "m0");
+}
+
+// The same with a wave-uniform 64-bit base and a 32-bit per-lane offset (the
+// saddr form), which keeps one VGPR per address instead of two.
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, const char* lds_dst) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_dst;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ void lds_load16(const void* gsrc, void* ldst) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
                                    (__attribute__((address_space(3))) void*)ldst, 16, 0, 0);
@@ -239,21 +263,22 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
   // base pointer of each of the tile's pages; otherwise the page is looked up
   // per round.
   auto k_round = [&](char* kl, const char* const* pp, auto pg, int j0, int r) {
-    const char* src;
-    if constexpr (PAGE16)
-      src = pp[(r * NW * KEYS_PER_LOAD) >> 4];
-    else
-      src = kbase_g + (int64_t)pg(kpg[r]) * page_bytes +
-            (KT < psize ? (j0 & (psize - 1)) * D * 2 : 0);
-    lds_load16(src + koff[r], kl + (r * NW + w) * 1024);
+    if constexpr (PAGE16) {
+      lds_dma16_s(pp[(r * NW * KEYS_PER_LOAD) >> 4], (uint32_t)koff[r], kl + (r * NW + w) * 1024);
+    } else {
+      const char* src = kbase_g + (int64_t)pg(kpg[r]) * page_bytes +
+                        (KT < psize ? (j0 & (psize - 1)) * D * 2 : 0);
+      lds_load16(src + koff[r], kl + (r * NW + w) * 1024);
+    }
   };
   auto v_round = [&](char* vl, const char* const* pp, auto pg, int j0, int r) {
-    const char* src;
-    if constexpr (PAGE16)
-      src = pp[(8 * ((r * NW * 64) / D)) >> 4];
-    else
-      src = vbase_g + (int64_t)pg(vpg[r]) * page_bytes + (KT < psize ? (j0 & (psize - 1)) * 2 : 0);
-    lds_load16(src + voff[r], vl + (r * NW + w) * 1024);
+    if constexpr (PAGE16) {
+      lds_dma16_s(pp[(8 * ((r * NW * 64) / D)) >> 4], (uint32_t)voff[r], vl + (r * NW + w) * 1024);
+    } else {
+      const char* src =
+          vbase_g + (int64_t)pg(vpg[r]) * page_bytes + (KT < psize ? (j0 & (psize - 1)) * 2 : 0);
+      lds_load16(src + voff[r], vl + (r * NW + w) * 1024);
+    }
   };
   // Copy of v made by an opaque move, issued where v's load is known to have
   // landed: later readlanes of the copy need no wait (the compiler cannot
@@ -454,16 +479,21 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
     }
   }
 
-  auto step = [&](auto ST, int it) {
+  // FULL: a step with a next tile and loads of V[t+1] and K[t+2], known at
+  // compile time, so that no MFMA or load of the step sits behind a branch
+  // (with run-time conditions the compiler also gave up tracking the LDS
+  // reads and waited for all of them before every MFMA)
+  auto step = [&](auto ST, int it, auto FULL) {
     constexpr int st = decltype(ST)::value;
+    constexpr bool full_c = decltype(FULL)::value;
     char* kfree = st ? k_lds1 : k_lds0;   // K[t] (used) -> K[t+2]
     char* knext = st ? k_lds0 : k_lds1;   // K[t+1]
     char* vcur = st ? v_lds1 : v_lds0;    // V[t]
     char* vfree = st ? v_lds0 : v_lds1;   // V[t-1] (used) -> V[t+1]
     const int j0 = (jt0 + it) * KT;
-    const bool has_next = it + 1 < ntiles;
-    const bool load_v = it + 1 < ntiles;
-    const bool load_k = it + 2 < ntiles;
+    const bool has_next = full_c || it + 1 < ntiles;
+    const bool load_v = full_c || it + 1 < ntiles;
+    const bool load_k = full_c || it + 2 < ntiles;
     // page ids of V[t+2] and K[t+3] for the next step (16-slot pages)
     const int pid_next = PAGE16 ? load_pids(it + 2, it + 3) : 0;
     auto pg_v = [&](int p) { return page_id(j0 + KT, p); };
@@ -560,12 +590,16 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
     for (int kb = 0; kb < KBLK; ++kb) s[kb] = s2[kb];
     if constexpr (PAGE16) pid = settled(pid_next);
   };
+  // steps with two more tiles after them in pairs (buffer parity is a
+  // template argument), then the last one to three tiles
   int it = 0;
-  for (; it + 1 < ntiles; it += 2) {
-    step(std::integral_constant<int, 0>{}, it);
-    step(std::integral_constant<int, 1>{}, it + 1);
+  for (; it + 3 < ntiles; it += 2) {
+    step(std::integral_constant<int, 0>{}, it, std::true_type{});
+    step(std::integral_constant<int, 1>{}, it + 1, std::true_type{});
   }
-  if (it < ntiles) step(std::integral_constant<int, 0>{}, it);
+  if (it < ntiles) step(std::integral_constant<int, 0>{}, it, std::false_type{});
+  if (it + 1 < ntiles) step(std::integral_constant<int, 1>{}, it + 1, std::false_type{});
+  if (it + 2 < ntiles) step(std::integral_constant<int, 0>{}, it + 2, std::false_type{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!row_valid) return;

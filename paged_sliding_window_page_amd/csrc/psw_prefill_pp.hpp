@@ -35,29 +35,6 @@
 namespace psw_dev {
 namespace {
 
-// global_load_lds_dwordx4 issued as inline assembly: 16 bytes per lane from
-// gsrc into LDS at lds_base + 16 * lane.  The tile buffers are picked at run
-// time, so the compiler could not tell these writes from the MFMA operand
-// reads of other buffers and would wait for every one of them before each
-// read; the kernel orders them itself with explicit vmcnt waits and barriers.
-__device__ __forceinline__ void lds_dma16(const void* gsrc, const char* lds_dst) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_dst;
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gsrc), "s"(m0)
-               : "memory", "m0");
-}
-
-// The same with a wave-uniform 64-bit base and a 32-bit per-lane offset (the
-// saddr form), which keeps one VGPR per address instead of two.
-__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, const char* lds_dst) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_dst;
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(m0)
-               : "memory", "m0");
-}
-
 // A copy of v the compiler cannot see through (values derived from it are
 // recomputed where they are used instead of being held in registers).
 __device__ __forceinline__ int opaque(int v) {
