@@ -152,8 +152,11 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
   __shared__ __attribute__((aligned(1024))) char k_lds1[TILE];
   __shared__ __attribute__((aligned(1024))) char v_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) char v_lds1[TILE];
-  // partial S^T of each wave, [wave][register quad][lane] (conflict-free)
-  __shared__ f32x4 xs[DH > 1 ? NW : 1][4 * KBLK][64];
+  // partial S^T of each wave, [step parity][wave][register quad][lane]
+  // (conflict-free); two copies, so that a wave writes the next tile's while
+  // its partner may still be reading the previous step's, with no barrier
+  // between them
+  __shared__ f32x4 xs[2][DH > 1 ? NW : 1][4 * KBLK][64];
 
   const int lane = threadIdx.x & 63;
   // wave index, explicitly wave-uniform so that per-wave address math is scalar
@@ -292,7 +295,8 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
   auto tile_pages = [&](const char* base, auto pg, const char** pp) {
     if constexpr (PAGE16) {
 #pragma unroll
-      for (int p = 0; p < NPP; ++p) pp[p] = base + (int64_t)pg(p) * page_bytes;
+      for (int p = 0; p < NPP; ++p)  // 32-bit factors: pages are below 4 GiB
+        pp[p] = base + (uint64_t)(uint32_t)pg(p) * (uint32_t)page_bytes;
     }
   };
   auto issue_k = [&](char* kl, int j0, auto pg) {
@@ -370,15 +374,21 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
   auto tile_max = [&](f32x16* s, bool masked, int j0) {
     float mx = -__builtin_inff();
     if (!masked) {
-      float hi = -__builtin_inff(), lo = __builtin_inff();
+      // max of s * c2: c2 times the max of s, or of the min for a negative c2
+      float e = s[0][0];
+      if (c2 >= 0.0f) {
 #pragma unroll
-      for (int kb = 0; kb < KBLK; ++kb)
+        for (int kb = 0; kb < KBLK; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          hi = fmaxf(hi, s[kb][r]);
-          lo = fminf(lo, s[kb][r]);
-        }
-      mx = c2 >= 0.0f ? hi * c2 : lo * c2;
+          for (int r = 0; r < 16; ++r) e = fmaxf(e, s[kb][r]);
+      } else {
+        rare_path();
+#pragma unroll
+        for (int kb = 0; kb < KBLK; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) e = fminf(e, s[kb][r]);
+      }
+      mx = e * c2;
     } else {
       rare_path();
       const int kb0 = j0 + 8 * h - lo_n;
@@ -417,17 +427,17 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
           kl + (kaddr0 ^ ((ks & 7) << 5)) + (ks >> 3) * 256 + kb * 32 * NCH * 16 + kdh);
   };
   // partial scores of the other dim half (head_dim 512): write, barrier, add
-  auto xs_put = [&](const f32x16* sacc) {
+  auto xs_put = [&](const f32x16* sacc, int xb) {
     if constexpr (DH > 1) {
 #pragma unroll
       for (int kb = 0; kb < KBLK; ++kb)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          xs[w][4 * kb + c][lane] = f32x4{sacc[kb][4 * c], sacc[kb][4 * c + 1],
-                                          sacc[kb][4 * c + 2], sacc[kb][4 * c + 3]};
+          xs[xb][w][4 * kb + c][lane] = f32x4{sacc[kb][4 * c], sacc[kb][4 * c + 1],
+                                              sacc[kb][4 * c + 2], sacc[kb][4 * c + 3]};
     }
   };
-  auto xs_add = [&](f32x16* sacc) {
+  auto xs_add = [&](f32x16* sacc, int xb) {
     // a + b is the same float in both waves of a pair, so both run identical
     // softmaxes
     if constexpr (DH > 1) {
@@ -435,7 +445,7 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
       for (int kb = 0; kb < KBLK; ++kb)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const f32x4 o = xs[w ^ RG][4 * kb + c][lane];
+          const f32x4 o = xs[xb][w ^ RG][4 * kb + c][lane];
 #pragma unroll
           for (int i = 0; i < 4; ++i) sacc[kb][4 * c + i] += o[i];
         }
@@ -473,9 +483,9 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (DH > 1) {
-      xs_put(s);
+      xs_put(s, 1);
       lds_barrier();
-      xs_add(s);
+      xs_add(s, 1);
     }
   }
 
@@ -577,15 +587,15 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
       constexpr int PER = NT * DB / ROUNDS;
       if (i % PER == 0 && load_k) k_round(kfree, kpp, pg_k, j0 + 2 * KT, i / PER);
     });
-    // hand over: tile t+1's partial scores to the partner wave (after every
-    // wave has read the previous ones), this wave's loads landed and zeroed
-    // past kv_len, then the barrier
-    if constexpr (DH > 1) lds_barrier();
-    xs_put(s2);
+    // hand over: tile t+1's partial scores to the partner wave (the copy of
+    // this step's parity: the partner read it two steps back, before the
+    // last barrier), this wave's loads landed and zeroed past kv_len, then
+    // the barrier
+    xs_put(s2, st);
     __builtin_amdgcn_s_waitcnt(0);
     if (load_v) sanitize(vfree, j0 + KT);
     __syncthreads();
-    xs_add(s2);
+    xs_add(s2, st);
 #pragma unroll
     for (int kb = 0; kb < KBLK; ++kb) s[kb] = s2[kb];
     if constexpr (PAGE16) pid = settled(pid_next);
