@@ -7,8 +7,9 @@
 // itself; the pieces of a request cut between work-groups write an
 // unnormalised partial (o, running max in log2 units, sum) to their slot and
 // merge_kernel combines them.  The host cuts the batch's keys into equal
-// contiguous shares, one per resident work-group, so every work-group streams
-// the same number of tiles and the launch ends together.
+// contiguous shares, one per work-group and at most four waves' worth per CU
+// (all of them resident at once), so every work-group streams the same number
+// of tiles and the launch ends together.
 //
 // Decode streams every K/V byte once and uses it for at most 16 query rows,
 // so the kernel is laid out for the memory stream, not for the matrix cores:

@@ -56,7 +56,8 @@ static int check_case(const PlanState& st, int64_t wl, int32_t mode, const Decod
     for (int g = 0; g < ds.num_wgs; ++g)
       if (ds.wg_items[g] >= ds.wg_items[g + 1]) return 13;  // every work-group has an item
     if (!ds.direct || mode == PSW_DECODE_SPLIT) {
-      // split form: at most the resident work-groups, shares within one unit
+      // split form: at most kDecodeResidentWaves' worth of work-groups,
+      // shares within one unit
       if (int64_t(ds.num_wgs) * (st.head_dim / 128) * st.num_kv_heads >
           std::max<int64_t>(kDecodeResidentWaves, (st.head_dim / 128) * st.num_kv_heads))
         return 14;
