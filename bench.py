@@ -13,8 +13,8 @@ workload (inputs resident in HBM before timing starts), all on one stream:
   decode_global_hd512  the same requests on the global family, full attention
 
 Each kernel launch is bracketed by HIP events on that stream; a 1 GiB buffer is
-rewritten before every HBM-bound row (outside its events) so its bytes come
-from HBM, not from the 256 MB last-level cache.
+read before every HBM-bound row (outside its events) so its bytes come from
+HBM, not from the 256 MB last-level cache.
 
 The JSON line's `value` is the windowed paged prefill's algorithmic TFLOP/s on
 the batch-8 workload (only (query, key) pairs inside the window count).  Per-row
