@@ -235,9 +235,9 @@ int paged_prefill_hd512(psw_plan* plan, const psw_pool* pool, int64_t layer,
  * every request (PSW_E_SHAPE otherwise) and are otherwise identical to
  * paged_prefill_window_hd256 / paged_prefill_hd512.
  * Two forms, chosen per call by the plan's decode mode:
- *   PSW_DECODE_SPLIT   the batch's keys (64-key units) laid end to end and
- *                      cut into equal shares, one per work-group (as many as
- *                      are resident at once, at least one per request, at
+ *   PSW_DECODE_SPLIT   the batch's keys (32-key units) laid end to end and
+ *                      cut into equal shares, one per work-group (at most
+ *                      four waves' worth per CU, at least one per request, at
  *                      most one per unit); a request inside one share is
  *                      written directly, the pieces of a request cut between
  *                      shares write fp32 partials to the plan's workspace and

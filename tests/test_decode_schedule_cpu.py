@@ -1,10 +1,10 @@
 """Host-side invariants of the decode schedule, checked by a small C++ program
 compiled here with g++ against the library's host source (no GPU, no HIP
 runtime): key ranges covered exactly once per request, pieces inside their
-request and on 64-key boundaries, consecutive partial slots per request,
-direct writes only for whole requests in the decode kernel, and equal shares
-across the split form's work-groups (3000 random batches, windows, groups and
-forms)."""
+request and on 32-key (one decode tile) boundaries, consecutive partial slots
+per request, direct writes only for whole requests in the decode kernel, and
+equal shares across the split form's work-groups (3000 random batches,
+windows, groups and forms)."""
 import os
 import shutil
 import subprocess
