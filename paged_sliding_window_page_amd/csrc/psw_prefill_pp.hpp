@@ -423,7 +423,15 @@ __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
     // 2j), or K(0) before the first phase
     if (j >= 0) preload(std::true_type{}, V0, K0);
     else preload(std::false_type{}, V1, K0);
-    lds_barrier();
+    // barrier with those three operand reads still in flight (lgkmcnt(3)):
+    // LDS accesses complete in order, so every earlier one (the V zeroing
+    // above) is done, and the buffers they read, V(j) and K(j+1), are not
+    // refilled in the next slot.  Nor does the barrier wait for the scalar
+    // page-id loads of this phase.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc37f);  // lgkmcnt(3); vmcnt and expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
   // MFMA(u): PV(u-1) from V(u-1) (if u >= 1), QK(u) from K(u) (if u <
   // ntiles), operands preloaded.  Group 0 then loads K(u+2) into the buffer
