@@ -28,7 +28,7 @@ pages are silent, and which parts are pinned by tests and which are conventions
 eps, and the RoPE pairing, whose frequency schedule and pairing are pinned only
 against a library routine).
 """
-from .bf16 import bf16_bits, bits_to_f64, to_f64, f64_to_bf16_bits, ulp_bf16
+from .bf16 import bf16_bits, bits_to_f64, to_f64, f64_to_bf16_bits
 from .layout import PoolGeometry, kv_blocks, gather_kv, kv_lengths
 from .attention import paged_attention, attention_rows, allowed_keys
 from .prep import (inv_rms, rms_norm_weighted, rope_rotate_half, qkv_prep_hd256,
@@ -36,7 +36,7 @@ from .prep import (inv_rms, rms_norm_weighted, rope_rotate_half, qkv_prep_hd256,
                    apply_pool_writes)
 
 __all__ = [
-    "bf16_bits", "bits_to_f64", "to_f64", "f64_to_bf16_bits", "ulp_bf16",
+    "bf16_bits", "bits_to_f64", "to_f64", "f64_to_bf16_bits",
     "PoolGeometry", "kv_blocks", "gather_kv", "kv_lengths",
     "paged_attention", "attention_rows", "allowed_keys",
     "inv_rms", "rms_norm_weighted", "rope_rotate_half", "qkv_prep_hd256",

@@ -56,9 +56,3 @@ def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
         r = np.where(nan, np.uint16(0x7FC0), r)
     return r
 
-
-def ulp_bf16(x: np.ndarray) -> np.ndarray:
-    """Spacing of bf16 numbers at |x| (8 significant bits)."""
-    a = np.abs(np.asarray(x, dtype=np.float64))
-    e = np.floor(np.log2(np.maximum(a, np.finfo(np.float32).tiny)))
-    return np.exp2(e - 7.0)

@@ -156,24 +156,16 @@ def test_fp32_and_bf16_outputs_agree():
         b16.astype(np.float32))
 
 
-def test_batch8_windowed_prefill_full_size_sampled():
+def test_batch8_windowed_prefill_full_size():
     """8 requests, lengths ~ U[128, 2048] at start 0, pool of 4096 pages with
-    random non-overlapping tables, window_left 1023: every row of the shortest
-    request plus 200 random (token, head) rows of the rest against the oracle."""
+    random non-overlapping tables, window_left 1023, in the launch the benchmark
+    times: the whole output tensor against the oracle."""
     g = synth.generator(2)
     lens = synth.uniform_lengths(8, 128, 2048, g)
     case = _local(2, lens, lens, num_pages=4096)
     gpu = run_attention(case, window_left=1023, label="b8 full size")
-    rng = np.random.default_rng(2)
-    total = sum(lens)
-    samples = [(int(t), int(h)) for t, h in zip(rng.integers(0, total, 200),
-                                                rng.integers(0, 16, 200))]
-    short = int(np.argmin(lens))
-    q0 = int(case.qo_indptr[short])
-    samples += [(q0 + i, h) for i in range(lens[short]) for h in range(16)]
-    ref = oracle_attention(case, window_left=1023, samples=samples)
-    idx = tuple(np.array(samples).T)
-    check_close(gpu[idx], ref[idx], "b8 sampled")
+    ref = oracle_attention(case, window_left=1023, threads=8)
+    check_close(gpu, ref, "b8 whole tensor")
 
 
 # ------------------------------------------------ hd512 full prefill ----
@@ -203,17 +195,33 @@ def test_hd512_full_prefill(qo, kv):
     check_close(gpu, oracle_attention(case), f"hd512 {qo}")
 
 
-def test_hd512_full_size_sampled():
-    """4 requests x 4096 tokens, causal, pool of 2048 pages: 160 sampled rows."""
+@pytest.mark.parametrize("page_size", [8, 32, 64])
+def test_hd512_page_sizes(page_size):
+    """Page sizes other than 16 (per-round page lookup, a tile spanning part of
+    a page or several pages)."""
+    case = _global_case(39, [90, 33, 1], [150, 200, 77], page_size=page_size)
+    gpu = run_attention(case, label=f"hd512 P={page_size}")
+    check_close(gpu, oracle_attention(case), f"hd512 P={page_size}")
+
+
+@pytest.mark.parametrize("page_size", [16, 32])
+def test_hd512_fp32_output(page_size):
+    case = _global_case(47, [100, 7], [230, 64], page_size=page_size)
+    f32 = run_attention(case, out_dtype=torch.float32, label=f"hd512 fp32 P={page_size}")
+    check_close(f32, oracle_attention(case), f"hd512 fp32 P={page_size}")
+    b16 = run_attention(case, out_dtype=torch.bfloat16, label=f"hd512 bf16 P={page_size}")
+    np.testing.assert_array_equal(
+        torch.from_numpy(f32).to(torch.float32).to(torch.bfloat16).float().numpy(),
+        b16.astype(np.float32))
+
+
+def test_hd512_full_size():
+    """4 requests x 4096 tokens, causal, pool of 2048 pages, in the launch the
+    benchmark times: the whole output tensor (262144 rows) against the oracle."""
     case = _global_case(3, [4096] * 4, [4096] * 4, num_pages=2048)
     gpu = run_attention(case, label="hd512 4x4096")
-    rng = np.random.default_rng(3)
-    samples = [(int(t), int(h)) for t, h in zip(rng.integers(0, 4 * 4096, 150),
-                                                rng.integers(0, 16, 150))]
-    samples += [(0, 0), (4095, 15), (4096, 3), (16383, 7)]
-    ref = oracle_attention(case, samples=samples)
-    idx = tuple(np.array(samples).T)
-    check_close(gpu[idx], ref[idx], "hd512 sampled")
+    ref = oracle_attention(case, threads=4)
+    check_close(gpu, ref, "hd512 whole tensor")
 
 
 # ------------------------------------------------ decode via the prefill entry ----
