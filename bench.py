@@ -6,6 +6,9 @@ workload (inputs resident in HBM before timing starts), all on one stream:
   prep_hd256           fused Q/K/V norm+RoPE+scatter, 8192 tokens, layer 3 of 8
   prep_hd512           fused K/V (V = weightless norm of raw K), 8192 tokens
   prep_q_hd512         the global family's Q norm+RoPE, 8192 tokens x 16 heads
+  prefill_window_hd256_1x64
+                       windowed paged prefill, one request of 64 tokens, 32-page
+                       pool, window 1023, fp32 output (launch-latency bound)
   prefill_window_hd256 windowed paged prefill, 8 requests ~ U[128, 2048], window 1023
   prefill_hd512        full paged prefill, 4 x 4096 tokens, 16 Q / 1 KV heads
   decode_local_hd256   one-token decode through the prefill entry, 64 requests,
@@ -259,6 +262,24 @@ def build_rows(torch, psw, synth, dev, want):
                         "query prep hd512, 8192 tokens x 16 heads at start 0, RoPE theta 1e4 "
                         "over 16384 positions", hbm=True))
 
+    # ---- windowed prefill hd256, one request of 64 tokens, fp32 output ----
+    if "prefill_window_hd256_1x64" in want:
+        case = synth.attention_case(1, [64], [64], num_pages=32, **synth.LOCAL)
+        pool = case.pool.to(dev)
+        q = case.q.to(dev)
+        o = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        plan = plan_of(case.qo_indptr, case.table, 16, 8, 256, 32)
+        pd = psw.pool_desc(pool, num_layers=1, num_pages=32, page_size=16, num_kv_heads=8,
+                           head_dim=256)
+
+        def run(plan=plan, pd=pd, q=q, o=o):
+            psw.paged_prefill_window_hd256(plan, pd, 0, q, 1.0, 1023, o)
+        rows.append(Row("prefill_window_hd256_1x64", run,
+                        attention_flops([64], [64], 16, 256, 1023), "TFLOP/s", "mfma",
+                        "hd256 windowed paged prefill, 1 request of 64 tokens at start 0, "
+                        "16Q/8KV, page 16, pool 32 pages (random permutation), window_left "
+                        "1023, sm_scale 1, fp32 out"))
+
     # ---- windowed prefill hd256, batch 8 ----
     if "prefill_window_hd256" in want:
         lens = synth.uniform_lengths(8, 128, 2048, synth.generator(2))
@@ -328,14 +349,35 @@ def build_rows(torch, psw, synth, dev, want):
     return rows
 
 
-def cpu_baseline(synth, oracle, case, budget_s=12.0):
-    """fp64 oracle on whole requests of the batch-8 windowed workload until the
-    time budget is spent; returns algorithmic TFLOP/s on that sample."""
+def cpu_model():
+    """The host CPU's model string (first "model name" of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_threads():
+    """Threads the oracle's array library runs with (its BLAS pool)."""
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(synth, oracle, case, budget_s=12.0):
+    """fp64 oracle on whole requests of the batch-8 windowed workload until the
+    time budget is spent; returns algorithmic TFLOP/s on that sample.  The
+    oracle runs in numpy: its matrix products use the BLAS thread pool (sized
+    by the host's environment, e.g. OMP_NUM_THREADS), the rest one thread."""
+    import torch
+    cores = cpu_threads()
     g = oracle.PoolGeometry(1, case.num_pages, 8, 16, 256)
     done, flops = [], 0.0
     t0 = time.perf_counter()
@@ -352,7 +394,10 @@ def cpu_baseline(synth, oracle, case, budget_s=12.0):
     lens = [case.qo_lens[b] for b in done]
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{len(done)} of 8 requests of the batch-8 windowed workload "
-                      f"(seq_len {lens}), all 16 heads, fp64, {dt:.1f} s"}
+                      f"(seq_len {lens}), all 16 heads, fp64, {dt:.1f} s",
+            "wall_s": round(dt, 3), "os_cpu_count": os.cpu_count(),
+            "torch_threads": torch.get_num_threads(), "blas_threads": int(cores),
+            "cpu_model": cpu_model()}
 
 
 def decode_sweep():
@@ -437,8 +482,9 @@ def main():
     import synth
     import paged_sliding_window_page_amd as psw
 
-    all_rows = ["prep_hd256", "prep_hd512", "prep_q_hd512", "prefill_window_hd256",
-                "prefill_hd512", "decode_local_hd256", "decode_global_hd512"]
+    all_rows = ["prep_hd256", "prep_hd512", "prep_q_hd512", "prefill_window_hd256_1x64",
+                "prefill_window_hd256", "prefill_hd512", "decode_local_hd256",
+                "decode_global_hd512"]
     want = set(args.rows.split(",")) if args.rows else set(all_rows)
     dev = torch.device("cuda", 0)
     # cache flush before every HBM-bound row: a 1 GiB read evicts the L2s and

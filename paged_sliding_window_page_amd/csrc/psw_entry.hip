@@ -9,11 +9,22 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstring>
 #include <string>
 #include <vector>
 
 #include "psw_device.hpp"
 #include "psw_host.hpp"
+
+// Pinned host staging of one metadata upload.  A copy from pinned memory is
+// asynchronous, so an entry never waits on the host for its uploads; a slot
+// is refilled only once the event recorded behind its copy has completed.
+struct psw_stage_slot {
+  int32_t* host = nullptr;
+  size_t cap = 0;  // bytes
+  hipEvent_t ev = nullptr;
+  bool busy = false;
+};
 
 struct psw_device_mirror {
   int device = -1;
@@ -39,9 +50,8 @@ struct psw_device_mirror {
   float* part = nullptr;
   size_t part_cap = 0;
   int32_t* err = nullptr;  // [4]: flag, page, position, spare
-  std::vector<int32_t> st_meta, st_pf, st_dc, st_req, st_prep;
-  hipEvent_t ev = nullptr;
-  bool ev_pending = false;
+  std::vector<psw_stage_slot> slots;
+  std::vector<int32_t*> retired;  // outgrown pinned buffers, freed with the mirror
 };
 
 namespace {
@@ -58,43 +68,75 @@ int hip_fail(hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_fail(e_, #call);  \
   } while (0)
 
-// Host staging buffers are the sources of asynchronous copies: wait for the
-// previous upload before reusing any of them.
-int wait_staging(psw_device_mirror* m) {
-  if (m->ev_pending) {
-    PSW_HIP(hipEventSynchronize(m->ev));
-    m->ev_pending = false;
+// Most uploads that may be in flight at once before an upload waits for the
+// oldest (a serving loop has one or two: the previous step's and its own).
+constexpr size_t kMaxStageSlots = 16;
+
+// A staging slot of at least `bytes` whose previous copy has completed.
+int acquire_slot(psw_device_mirror* m, size_t bytes, psw_stage_slot** out) {
+  psw_stage_slot* pick = nullptr;
+  for (psw_stage_slot& sl : m->slots) {
+    if (sl.busy) {
+      const hipError_t q = hipEventQuery(sl.ev);
+      if (q == hipSuccess) sl.busy = false;
+      else if (q != hipErrorNotReady) return hip_fail(q, "hipEventQuery");
+    }
+    if (!sl.busy && (!pick || sl.cap >= bytes)) pick = &sl;
   }
+  if (!pick && m->slots.size() < kMaxStageSlots) {
+    psw_stage_slot sl;
+    PSW_HIP(hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming));
+    m->slots.push_back(sl);
+    pick = &m->slots.back();
+  }
+  if (!pick) {
+    // every slot still in flight: the only wait, on the oldest upload
+    pick = &m->slots.front();
+    PSW_HIP(hipEventSynchronize(pick->ev));
+    pick->busy = false;
+  }
+  if (pick->cap < bytes) {
+    if (pick->host) m->retired.push_back(pick->host);  // its last copy has completed
+    pick->host = nullptr;
+    pick->cap = 0;
+    const size_t want = bytes < 4096 ? 4096 : bytes + bytes / 2;
+    PSW_HIP(hipHostMalloc(reinterpret_cast<void**>(&pick->host), want, hipHostMallocDefault));
+    pick->cap = want;
+  }
+  *out = pick;
   return PSW_OK;
 }
 
+// Device buffer of at least `bytes`.  Growth is stream-ordered: the old
+// buffer is released after the work already queued on the stream, the new one
+// allocated in stream order, and the host never waits.
 template <typename T>
 int ensure(T** p, size_t* cap, size_t bytes, hipStream_t s) {
   if (bytes <= *cap && *p) return PSW_OK;
   if (*p) {
-    PSW_HIP(hipStreamSynchronize(s));  // work queued on the old buffer must finish
-    PSW_HIP(hipFree(*p));
+    PSW_HIP(hipFreeAsync(*p, s));
     *p = nullptr;
     *cap = 0;
   }
   const size_t want = bytes < 256 ? 256 : bytes;
-  PSW_HIP(hipMalloc(reinterpret_cast<void**>(p), want));
+  PSW_HIP(hipMallocAsync(reinterpret_cast<void**>(p), want, s));
   *cap = want;
   return PSW_OK;
 }
 
-int upload(psw_device_mirror* m, int32_t** dptr, size_t* cap, std::vector<int32_t>& stage,
-           const std::vector<int32_t>& src, hipStream_t s) {
-  int rc = wait_staging(m);
-  if (rc) return rc;
+int upload(psw_device_mirror* m, int32_t** dptr, size_t* cap, const std::vector<int32_t>& src,
+           hipStream_t s) {
   const size_t bytes = (src.empty() ? 1 : src.size()) * sizeof(int32_t);
-  rc = ensure(dptr, cap, bytes, s);
+  int rc = ensure(dptr, cap, bytes, s);
   if (rc) return rc;
-  stage = src;
-  if (stage.empty()) stage.push_back(0);
-  PSW_HIP(hipMemcpyAsync(*dptr, stage.data(), bytes, hipMemcpyHostToDevice, s));
-  PSW_HIP(hipEventRecord(m->ev, s));
-  m->ev_pending = true;
+  psw_stage_slot* sl = nullptr;
+  rc = acquire_slot(m, bytes, &sl);
+  if (rc) return rc;
+  if (src.empty()) sl->host[0] = 0;
+  else std::memcpy(sl->host, src.data(), bytes);
+  PSW_HIP(hipMemcpyAsync(*dptr, sl->host, bytes, hipMemcpyHostToDevice, s));
+  PSW_HIP(hipEventRecord(sl->ev, s));
+  sl->busy = true;
   return PSW_OK;
 }
 
@@ -105,15 +147,10 @@ int ensure_mirror(psw_plan* plan) {
   if (!plan->mirror) {
     psw_device_mirror* m = psw_mirror_new();
     m->device = dev;
-    hipError_t e = hipEventCreateWithFlags(&m->ev, hipEventDisableTiming);
-    if (e != hipSuccess) {
-      psw_mirror_free(m);
-      return hip_fail(e, "hipEventCreateWithFlags");
-    }
-    e = hipMalloc(reinterpret_cast<void**>(&m->err), 4 * sizeof(int32_t));
+    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&m->err), 4 * sizeof(int32_t), s);
     if (e == hipSuccess) e = hipMemsetAsync(m->err, 0, 4 * sizeof(int32_t), s);
     if (e != hipSuccess) {
-      psw_mirror_free(m);
+      psw_mirror_free(m, plan->stream);
       return hip_fail(e, "device error word");
     }
     plan->mirror = m;
@@ -132,7 +169,7 @@ int ensure_mirror(psw_plan* plan) {
     meta.insert(meta.end(), st.kv_page_indices.begin(), st.kv_page_indices.end());
     m->off_kvlen = meta.size();
     meta.insert(meta.end(), st.kv_len.begin(), st.kv_len.end());
-    int rc = upload(m, &m->meta, &m->meta_cap, m->st_meta, meta, s);
+    int rc = upload(m, &m->meta, &m->meta_cap, meta, s);
     if (rc) return rc;
     m->meta_gen = plan->generation;
   }
@@ -188,13 +225,18 @@ int run_attention(psw_plan* plan, const psw_pool* pool, int64_t layer, const voi
   psw_device_mirror* m = plan->mirror;
   psw_dev::AttnParams p{};
   int n_items = 0;
+  // the group-32 decode runs the split mode of the attention kernel, whose
+  // every work item writes a partial
+  const bool split_kernel = decode && st.group > psw_dev::kDecodeMaxGroup;
   if (decode) {
     if (m->dc_gen != plan->generation || m->dc_wl != wle || m->dc_mode != dmode) {
+      rc = psw::check_decode_items(st, plan->decode, split_kernel);
+      if (rc) return rc;
       // items, then the work-groups' item offsets
       std::vector<int32_t> table(plan->decode.items);
       table.insert(table.end(), plan->decode.wg_items.begin(), plan->decode.wg_items.end());
-      rc = upload(m, &m->dc_items, &m->dc_cap, m->st_dc, table, s);
-      if (!rc) rc = upload(m, &m->dc_req, &m->dc_req_cap, m->st_req, plan->decode.req_splits, s);
+      rc = upload(m, &m->dc_items, &m->dc_cap, table, s);
+      if (!rc) rc = upload(m, &m->dc_req, &m->dc_req_cap, plan->decode.req_splits, s);
       if (rc) return rc;
       m->dc_gen = plan->generation;
       m->dc_wl = wle;
@@ -214,7 +256,9 @@ int run_attention(psw_plan* plan, const psw_pool* pool, int64_t layer, const voi
     }
   } else {
     if (m->pf_gen != plan->generation || m->pf_wl != wle) {
-      rc = upload(m, &m->pf_items, &m->pf_cap, m->st_pf, plan->prefill.items, s);
+      rc = psw::check_prefill_items(st, plan->prefill);
+      if (rc) return rc;
+      rc = upload(m, &m->pf_items, &m->pf_cap, plan->prefill.items, s);
       if (rc) return rc;
       m->pf_gen = plan->generation;
       m->pf_wl = wle;
@@ -236,8 +280,10 @@ int run_attention(psw_plan* plan, const psw_pool* pool, int64_t layer, const voi
   p.group_shift = group_shift_of(st.group);
   p.window_left = static_cast<int32_t>(wle);
   p.scale_log2 = sm_scale * 1.4426950408889634f;
+  if ((split_kernel || (decode && plan->decode.num_partials > 0)) && !p.part_o)
+    return fail(PSW_E_PLAN, "the schedule writes partials but no workspace backs them");
   hipError_t e;
-  if (decode && st.group <= psw_dev::kDecodeMaxGroup)
+  if (decode && !split_kernel)
     e = psw_dev::launch_decode(head_dim, p, plan->decode.num_wgs * st.num_kv_heads, s);
   else
     e = head_dim == 256 ? psw_dev::launch_attention_d256(decode, o_dtype == 1, p, n_items, s)
@@ -263,6 +309,8 @@ int prepare_prep(psw_plan* plan, const psw_pool* pool, int64_t layer, const floa
                  psw_dev::PrepParams* p) {
   if (!plan->prep_built) {
     psw::build_prep_items(plan->st, &plan->prep_items);
+    int rc = psw::check_prep_items(plan->st, plan->prep_items);
+    if (rc) return rc;
     plan->prep_built = true;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(plan->stream);
@@ -270,7 +318,7 @@ int prepare_prep(psw_plan* plan, const psw_pool* pool, int64_t layer, const floa
   if (rc) return rc;
   psw_device_mirror* m = plan->mirror;
   if (m->prep_gen != plan->generation) {
-    rc = upload(m, &m->prep, &m->prep_cap, m->st_prep, plan->prep_items, s);
+    rc = upload(m, &m->prep, &m->prep_cap, plan->prep_items, s);
     if (rc) return rc;
     m->prep_gen = plan->generation;
   }
@@ -293,14 +341,20 @@ int prepare_prep(psw_plan* plan, const psw_pool* pool, int64_t layer, const floa
 
 psw_device_mirror* psw_mirror_new() { return new psw_device_mirror(); }
 
-void psw_mirror_free(psw_device_mirror* m) {
+void psw_mirror_free(psw_device_mirror* m, psw_stream_t stream) {
   if (!m) return;
-  if (m->ev_pending) (void)hipEventSynchronize(m->ev);
-  (void)hipDeviceSynchronize();
+  // the plan's work is ordered on its stream: once it has drained, no kernel
+  // or copy uses the buffers below
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipStreamSynchronize(s);
   for (void* p : {(void*)m->meta, (void*)m->pf_items, (void*)m->dc_items, (void*)m->dc_req,
                   (void*)m->prep, (void*)m->part, (void*)m->err})
-    if (p) (void)hipFree(p);
-  if (m->ev) (void)hipEventDestroy(m->ev);
+    if (p) (void)hipFreeAsync(p, s);
+  for (psw_stage_slot& sl : m->slots) {
+    if (sl.host) (void)hipHostFree(sl.host);
+    if (sl.ev) (void)hipEventDestroy(sl.ev);
+  }
+  for (int32_t* h : m->retired) (void)hipHostFree(h);
   delete m;
 }
 
@@ -393,6 +447,8 @@ int q_norm_rope_prefill_hd512(psw_plan* plan, const void* q_in, const void* q_no
   if (rc) return rc;
   if (!plan->prep_built) {
     psw::build_prep_items(plan->st, &plan->prep_items);
+    rc = psw::check_prep_items(plan->st, plan->prep_items);
+    if (rc) return rc;
     plan->prep_built = true;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(plan->stream);
@@ -400,7 +456,7 @@ int q_norm_rope_prefill_hd512(psw_plan* plan, const void* q_in, const void* q_no
   if (rc) return rc;
   psw_device_mirror* m = plan->mirror;
   if (m->prep_gen != plan->generation) {
-    rc = upload(m, &m->prep, &m->prep_cap, m->st_prep, plan->prep_items, s);
+    rc = upload(m, &m->prep, &m->prep_cap, plan->prep_items, s);
     if (rc) return rc;
     m->prep_gen = plan->generation;
   }

@@ -374,6 +374,82 @@ void build_prep_items(const PlanState& st, std::vector<int32_t>* out) {
   }
 }
 
+static int bad_item(const char* what, size_t i, const std::string& why) {
+  return fail(PSW_E_PLAN, std::string(what) + " item " + std::to_string(i) + ": " + why);
+}
+
+int check_prefill_items(const PlanState& st, const PrefillSchedule& ps) {
+  if (ps.items.size() % 4) return fail(PSW_E_PLAN, "prefill schedule is not made of quads");
+  for (size_t i = 0; i < ps.items.size() / 4; ++i) {
+    const int32_t b = ps.items[4 * i], t0 = ps.items[4 * i + 1];
+    const int32_t k0 = ps.items[4 * i + 2], k1 = ps.items[4 * i + 3];
+    if (b < 0 || b >= st.batch) return bad_item("prefill", i, "request out of range");
+    const int32_t qo = st.qo_indptr[b + 1] - st.qo_indptr[b];
+    if (t0 < 0 || t0 >= qo || t0 % ps.tile_q)
+      return bad_item("prefill", i, "first query token outside the request or off the tile");
+    if (k0 < 0 || k0 > k1 || k1 >= st.kv_len[b])
+      return bad_item("prefill", i, "key range outside the request's keys");
+  }
+  return PSW_OK;
+}
+
+int check_decode_items(const PlanState& st, const DecodeSchedule& ds, bool split_kernel) {
+  if (ds.items.size() % 4) return fail(PSW_E_PLAN, "decode schedule is not made of quads");
+  const size_t n = ds.items.size() / 4;
+  if (ds.req_splits.size() != size_t(2) * st.batch)
+    return fail(PSW_E_PLAN, "decode schedule has no split list per request");
+  for (size_t i = 0; i < n; ++i) {
+    const int32_t b = ds.items[4 * i], sl = ds.items[4 * i + 1];
+    const int32_t k0 = ds.items[4 * i + 2], k1 = ds.items[4 * i + 3];
+    if (b < 0 || b >= st.batch) return bad_item("decode", i, "request out of range");
+    if (k0 < 0 || k0 > k1 || k1 >= st.kv_len[b])
+      return bad_item("decode", i, "key range outside the request's keys");
+    if (sl >= ds.num_partials || sl < -1)
+      return bad_item("decode", i, "partial slot outside the workspace");
+    if (sl < 0 && split_kernel)
+      return bad_item("decode", i, "the split attention kernel writes a partial for every item");
+  }
+  for (int32_t b = 0; b < st.batch; ++b) {
+    const int64_t f = ds.req_splits[2 * b], c = ds.req_splits[2 * b + 1];
+    if (c < 0 || (c > 0 && (f < 0 || f + c > ds.num_partials)))
+      return fail(PSW_E_PLAN, "decode split list of request " + std::to_string(b) +
+                                  " points outside the workspace");
+  }
+  if (!split_kernel) {
+    if (ds.wg_items.size() != size_t(ds.num_wgs) + 1 || ds.wg_items.front() != 0 ||
+        ds.wg_items.back() != int32_t(n))
+      return fail(PSW_E_PLAN, "decode work-group item lists do not cover the items");
+    for (int32_t g = 0; g < ds.num_wgs; ++g)
+      if (ds.wg_items[g] > ds.wg_items[g + 1])
+        return fail(PSW_E_PLAN, "decode work-group item lists are not in order");
+  } else if (int64_t(ds.num_wgs) != int64_t(n)) {
+    return fail(PSW_E_PLAN, "the split attention kernel runs one item per work-group");
+  }
+  return PSW_OK;
+}
+
+int check_prep_items(const PlanState& st, const std::vector<int32_t>& items) {
+  constexpr size_t kInts = 6, kMaxTokens = 16;
+  if (items.size() % kInts) return fail(PSW_E_PLAN, "prep items are not made of sextuples");
+  for (size_t i = 0; i < items.size() / kInts; ++i) {
+    const int32_t* it = items.data() + kInts * i;
+    const int32_t b = it[0], tok0 = it[1], n = it[2], page = it[3], slot = it[4], pos = it[5];
+    if (b < 0 || b >= st.batch) return bad_item("prep", i, "request out of range");
+    const int32_t qo = st.qo_indptr[b + 1] - st.qo_indptr[b];
+    const int64_t start = int64_t(st.kv_len[b]) - qo;
+    if (n < 1 || size_t(n) > kMaxTokens) return bad_item("prep", i, "token count outside [1, 16]");
+    if (pos < start || int64_t(pos) + n > st.kv_len[b])
+      return bad_item("prep", i, "positions outside the request's new tokens");
+    if (tok0 != st.qo_indptr[b] + (pos - start))
+      return bad_item("prep", i, "first token does not match its position");
+    if (slot != pos % st.page_size || slot + n > st.page_size)
+      return bad_item("prep", i, "slots leave the page");
+    if (page < 0 || page >= st.num_pages || page != st.page_of(b, pos))
+      return bad_item("prep", i, "page is not the request's page for its position");
+  }
+  return PSW_OK;
+}
+
 static int check_plan_vs_pool(const psw_plan* plan, const psw_pool* pool, int64_t layer,
                               psw_stream_t stream, int64_t want_head_dim) {
   if (!plan) return fail(PSW_E_NULL, "plan is NULL");
@@ -588,7 +664,7 @@ int psw_plan_update(psw_plan* plan, const psw_plan_desc* desc) {
 
 void psw_plan_destroy(psw_plan* plan) {
   if (!plan) return;
-  if (plan->mirror) psw_mirror_free(plan->mirror);
+  if (plan->mirror) psw_mirror_free(plan->mirror, plan->stream);
   delete plan;
 }
 

@@ -128,6 +128,15 @@ int32_t effective_decode_mode(const PlanState& st, int32_t mode);
 // position).
 void build_prep_items(const PlanState& st, std::vector<int32_t>* out);
 
+// Consistency of a schedule before its first launch: the kernels trust their
+// items (request, keys, slots, pages), so every field is checked here against
+// the plan.  PSW_OK, or PSW_E_PLAN with a message naming the item.
+int check_prefill_items(const PlanState& st, const PrefillSchedule& ps);
+// split_kernel: the schedule feeds the split mode of the attention kernel,
+// where every item writes a partial slot.
+int check_decode_items(const PlanState& st, const DecodeSchedule& ds, bool split_kernel);
+int check_prep_items(const PlanState& st, const std::vector<int32_t>& items);
+
 // Window normalisation: -1 when the window cannot exclude any key.
 int64_t effective_window(const PlanState& st, int64_t window_left);
 
@@ -153,7 +162,8 @@ int check_q_prep_call(const psw_plan* plan, int64_t want_head_dim, const void* q
 // Device mirror (defined in the HIP translation unit; opaque here).
 struct psw_device_mirror;
 psw_device_mirror* psw_mirror_new();
-void psw_mirror_free(psw_device_mirror* m);
+// Releases the mirror after the work queued on the plan's stream.
+void psw_mirror_free(psw_device_mirror* m, psw_stream_t stream);
 
 struct psw_plan {
   psw_stream_t stream = nullptr;

@@ -12,7 +12,7 @@
 
 #include "psw_host.hpp"
 
-void psw_mirror_free(psw_device_mirror*) {}  // the device mirror is not linked here
+void psw_mirror_free(psw_device_mirror*, psw_stream_t) {}  // the device mirror is not linked here
 
 using namespace psw;
 
