@@ -265,6 +265,23 @@ int paged_decode_window_hd256(psw_plan* plan, const psw_pool* pool, int64_t laye
 int paged_decode_hd512(psw_plan* plan, const psw_pool* pool, int64_t layer, const void* q,
                        float sm_scale, void* o, int32_t o_dtype, psw_stream_t stream);
 
+/* paged_decode_hd512 for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, checks, kernels and results as paged_decode_hd512, but the
+ * plan's metadata, the decode schedule and the split-KV partials go to a
+ * static device array of 32 MiB per GPU (held until the process ends) instead
+ * of the plan's device buffers: no hipMalloc, hipFree or other allocation.
+ * A batch whose metadata, schedule and partials need more than 32 MiB is
+ * rejected with PSW_E_RANGE; GQA groups above 16 with PSW_E_UNSUPPORTED.
+ * The metadata is copied from the plan's host memory (synchronously with
+ * respect to the host) whenever the GPU's array does not already hold this
+ * plan's state, window and mode.  Every call on one GPU shares that array and
+ * keeps the last call's contents: calls that overlap on one GPU (from other
+ * streams or threads) race and must be ordered by the caller. */
+int paged_decode_hd512_noalloc(psw_plan* plan, const psw_pool* pool, int64_t layer,
+                               const void* q, float sm_scale, void* o, int32_t o_dtype,
+                               psw_stream_t stream);
+
 /* ----------------------------------------------------------------- prep ---- */
 
 /* hd256 fused prep ([P2] Proposed Plan), one pass per token:

@@ -116,6 +116,9 @@ _decode256 = _sig("paged_decode_window_hd256", ctypes.c_int, c_vp, ctypes.POINTE
                   c_i64, c_vp, ctypes.c_float, c_i64, c_vp, c_i32, c_vp)
 _decode512 = _sig("paged_decode_hd512", ctypes.c_int, c_vp, ctypes.POINTER(PoolDesc), c_i64,
                   c_vp, ctypes.c_float, c_vp, c_i32, c_vp)
+_decode512_noalloc = _sig("paged_decode_hd512_noalloc", ctypes.c_int, c_vp,
+                          ctypes.POINTER(PoolDesc), c_i64, c_vp, ctypes.c_float, c_vp, c_i32,
+                          c_vp)
 _decode_mode = _sig("psw_plan_set_decode_mode", ctypes.c_int, c_vp, c_i32)
 _decode_form = _sig("psw_plan_decode_form", ctypes.c_int, c_vp, c_i64, c_i32p,
                     ctypes.POINTER(c_i64))
@@ -146,7 +149,8 @@ _dev_err = _sig("psw_plan_device_errors", ctypes.c_int, c_vp)
 EXPORTS = ["psw_last_error", "psw_version", "psw_check_pool", "psw_plan_create",
            "psw_plan_update", "psw_plan_destroy", "psw_plan_get_info", "psw_prefill_tile_q",
            "paged_prefill_window_hd256", "paged_prefill_hd512", "paged_decode_window_hd256",
-           "paged_decode_hd512", "psw_plan_set_decode_mode", "psw_plan_decode_form",
+           "paged_decode_hd512", "paged_decode_hd512_noalloc", "psw_plan_set_decode_mode",
+           "psw_plan_decode_form",
            "qkv_norm_rope_paged_prefill_hd256", "k_v_norm_rope_paged_prefill_hd512",
            "q_norm_rope_prefill_hd512", "psw_rope_tables", "psw_plan_device_errors",
            "psw_kv_server_create", "psw_kv_server_destroy", "psw_kv_server_free_pages",
@@ -325,6 +329,17 @@ def paged_decode_hd512(plan: "Plan", pool: PoolDesc, layer: int, q, sm_scale: fl
     _check(_decode512(plan.handle, ctypes.byref(pool), int(layer), _ptr(q), float(sm_scale),
                       _ptr(o), o_dtype,
                       plan.stream if stream is None else _stream_handle(stream)))
+
+
+def paged_decode_hd512_noalloc(plan: "Plan", pool: PoolDesc, layer: int, q, sm_scale: float, o,
+                               stream=None) -> None:
+    """paged_decode_hd512 with its workspace in the library's static device
+    array (no device allocation)."""
+    import torch
+    o_dtype = 1 if o.dtype == torch.bfloat16 else 0
+    _check(_decode512_noalloc(plan.handle, ctypes.byref(pool), int(layer), _ptr(q),
+                              float(sm_scale), _ptr(o), o_dtype,
+                              plan.stream if stream is None else _stream_handle(stream)))
 
 
 def qkv_norm_rope_paged_prefill_hd256(plan: Plan, pool: PoolDesc, layer: int, q_in, k_in, v_in,

@@ -434,3 +434,31 @@ def test_ring_prep_refuses_a_step_longer_than_its_ring():
 def test_mfma_clock_probe_rejects_null():
     # checked before any device call, so it runs without a GPU
     assert _code(lambda: psw._check(psw._mfma_clock(None, None))) == "PSW_E_NULL"
+
+
+# ------------------------------------------------------- allocation-free decode ----
+
+def test_noalloc_decode_refuses_a_batch_past_its_workspace():
+    """One request of 140M keys: its 8.75M page ids alone need 35 MB of the
+    32 MiB static workspace, so the call is refused before any HIP call."""
+    kv = 140_000_000
+    n_pages = (kv + 15) // 16
+    ids = np.arange(n_pages, dtype=np.int32)
+    plan = psw.Plan([0, 1], [0, n_pages], ids, [kv - (n_pages - 1) * 16], num_qo_heads=16,
+                    num_kv_heads=1, head_dim=512, page_size=16, num_pages=n_pages, stream=0)
+    pool = psw.pool_desc(FAKE, numel=n_pages * 2 * 16 * 512, num_layers=1, num_pages=n_pages,
+                         page_size=16, num_kv_heads=1, head_dim=512)
+    code = _code(lambda: psw._check(psw._decode512_noalloc(plan.handle, ctypes.byref(pool), 0, FAKE,
+                                                           1.0, FAKE, 1, 0)))
+    assert code == "PSW_E_RANGE"
+    assert "workspace" in psw.last_error()
+    plan.close()
+
+
+def test_noalloc_decode_rejects_like_the_allocating_entry():
+    plan = _plan(qo_indptr=[0, 5, 9])   # prefill batch: not a decode plan
+    pool = psw.pool_desc(FAKE, numel=4 * 2 * 8 * 16 * 256, num_layers=1, num_pages=4,
+                         page_size=16, num_kv_heads=8, head_dim=256)
+    code = _code(lambda: psw._check(psw._decode512_noalloc(plan.handle, ctypes.byref(pool), 0,
+                                                           FAKE, 1.0, FAKE, 1, 0)))
+    assert code == "PSW_E_PLAN"   # an hd256 plan on the hd512 entry
