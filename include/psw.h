@@ -199,8 +199,9 @@ int psw_plan_get_info(const psw_plan* plan, psw_plan_info* info);
 
 /* Tile-size query ([P1] Description: a plan tiled differently from what the
  * kernel derives for itself is refused rather than misread).  Query tokens per prefill
- * work-group for a GQA group and head_dim; positivity is checked in the i32
- * domain. */
+ * work-group for a GQA group and head_dim: 256 / group at head_dim 256 and
+ * 128 / group at head_dim 512 (query rows are tokens x the group's heads);
+ * positivity is checked in the i32 domain. */
 int psw_prefill_tile_q(int64_t group, int64_t head_dim, int32_t* tile_q);
 
 /* ----------------------------------------------------------- attention ---- */

@@ -22,7 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpsw.so")
 
 SOURCES = ["psw_host.cpp", "psw_kv.cpp", "psw_entry.hip", "psw_attn256.hip", "psw_attn512.hip",
-           "psw_prep.hip", "psw_decode.hip", "psw_clock.hip", "psw_noalloc.hip"]
+           "psw_prep.hip", "psw_decode.hip", "psw_clock.hip", "psw_noalloc.hip",
+           "psw_prefill512.hip"]
 
 
 def _hipcc() -> str:

@@ -117,6 +117,14 @@ __device__ __forceinline__ float max_with_partner_half(float x) {
   return fmaxf(lo, hi);
 }
 
+// A copy of v the compiler cannot see through (values derived from it are
+// recomputed where they are used instead of being held in registers).
+__device__ __forceinline__ int opaque(int v) {
+  int r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+  return r;
+}
+
 // Keep the compiler from if-converting a rare branch into straight-line code.
 __device__ __forceinline__ void rare_path() { asm volatile("" ::: "memory"); }
 

@@ -1,6 +1,7 @@
-// Instantiations of the paged attention kernels for head_dim 512.  Each
-// head_dim is its own translation unit so that it can be compiled with the
-// code-generation options that suit its register budget.
+// Instantiations of the paged attention kernel for head_dim 512 in its split-KV
+// form (one-token decode with a GQA group wider than the decode kernel's).
+// Each head_dim is its own translation unit so that it can be compiled with
+// the code-generation options that suit its register budget.
 #include "psw_attention.hpp"
 
 namespace psw_dev {
@@ -21,8 +22,9 @@ hipError_t launch_one(const AttnParams& p, int n_items, hipStream_t s) {
 hipError_t launch_attention_d512(bool split, bool out_bf16, const AttnParams& p, int n_items,
                                 hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
-  if (split) return out_bf16 ? launch_one<true, true>(p, n_items, s) : launch_one<true, false>(p, n_items, s);
-  return out_bf16 ? launch_one<false, true>(p, n_items, s) : launch_one<false, false>(p, n_items, s);
+  // prefill: its own kernel (psw_prefill512.hip); here the split-KV form
+  if (!split) return launch_prefill512(out_bf16, p, n_items, s);
+  return out_bf16 ? launch_one<true, true>(p, n_items, s) : launch_one<true, false>(p, n_items, s);
 }
 
 hipError_t launch_merge_d512(bool out_bf16, const MergeParams& p, int batch, hipStream_t s) {

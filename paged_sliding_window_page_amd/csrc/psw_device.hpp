@@ -112,6 +112,8 @@ hipError_t launch_attention_d256(bool split, bool out_bf16, const AttnParams& p,
                                  hipStream_t s);
 hipError_t launch_attention_d512(bool split, bool out_bf16, const AttnParams& p, int n_items,
                                  hipStream_t s);
+// head_dim-512 prefill: 128 query rows per work-group, all 512 dims per wave
+hipError_t launch_prefill512(bool out_bf16, const AttnParams& p, int n_items, hipStream_t s);
 // One-token decode kernel: n_wgs = work-groups x KV heads, each work-group
 // running its items (whole requests write O, pieces write the same partials
 // as the split attention kernels).  Needs H_q / H_kv <= kDecodeMaxGroup.

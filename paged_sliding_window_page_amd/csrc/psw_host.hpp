@@ -39,7 +39,7 @@ int check_pool(const psw_pool* pool, bool need_base);
 // Tiling decisions, shared by the plan (which records them) and the device
 // code (which was compiled for them).
 constexpr int kPrefillRows = 256;          // query rows (token x head) per work-group (head_dim 256)
-constexpr int kPrefillRows512 = 64;        // the same at head_dim 512 (dims split over wave pairs)
+constexpr int kPrefillRows512 = 128;       // the same at head_dim 512 (four waves of 32 rows)
 constexpr int kKvTile256 = 64;             // keys per prefill tile at head_dim 256
 constexpr int kKvTile512 = 32;             // keys per prefill tile at head_dim 512
 // Decode pieces start and end at multiples of this key index: one decode

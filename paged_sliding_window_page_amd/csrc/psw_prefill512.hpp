@@ -1,0 +1,565 @@
+// Full paged prefill at head_dim 512 (PR "feat(gemma4): paged KV serving
+// across both attention families", Description: the global family has one KV
+// head of 512 dims and attends to every earlier key; PR "feat(kernels): Rust
+// wrapper for the hd256 windowed paged prefill", Description: explicit
+// sm_scale, keys found through the page table and the final page's length).
+//
+// Work-group: 4 waves x 32 query rows = 128 rows = (128 / group) tokens x the
+// group's heads of one KV head, one work-group per CU.  Each wave owns all 512
+// dims of its rows: O^T (32 rows x 512 dims, fp32) fills the 256 accumulator
+// registers, Q (32 rows x 512 dims, bf16) 128 vector registers, so every
+// score feeds 64 MFMAs of its own wave and the softmax runs once per row.
+// Keys come in tiles of 32: K [32][512] and V^T [32 keys][512 dims], 32 KiB
+// each, in two K buffers and three V buffers (all 160 KiB of LDS), shared by
+// the 128 rows.
+//
+// Per wave and tile step t (between two work-group barriers):
+//   O^T  += V^T(t-1) P^T(t-1)     32 x v_mfma_f32_32x32x16_bf16
+//   S^T(t+1) = K(t+1) Q^T          32 x v_mfma_f32_32x32x16_bf16
+// with the LDS operand reads running three MFMAs ahead through one register
+// ring, and, interleaved with the 64 MFMAs, the softmax of S(t) into P(t)
+// (row max, lazily raised running max, exponentials, row sums) and this
+// wave's share of the loads of K(t+2) and V(t+1) (global_load_lds_dwordx4,
+// 16 bytes per lane straight into LDS).  A step ends by waiting for its own
+// loads, zeroing V keys past kv_len, reading the first operands of the next
+// step (V(t), published a step earlier) and the barrier; the V ring is three
+// deep so that those reads can precede the barrier and the matrix unit finds
+// its first operands ready after it.
+//
+// Operand layouts are those of the other attention kernels: K rows
+// XOR-swizzled on the 16-byte chunk index and read in the kperm order, so each
+// lane's S^T accumulators are exactly the 8 consecutive keys its P^T operand
+// needs; V^T dim-major chunks of 8 keys.
+#pragma once
+#include "psw_attention.hpp"
+
+namespace psw_dev {
+namespace {
+
+// The QK MFMAs as inline assembly with their accumulators in VGPRs, so that
+// the 256 accumulator registers hold O (the PV MFMAs, left to the compiler,
+// take the accumulator-register form) and the scores stay where the softmax
+// reads them.  The compiler does not see these as MFMAs, so the kernel keeps
+// the hardware's wait states itself: a dependent accumulation into the same
+// registers needs none, the chain's sources come from LDS reads (ordered by
+// lgkmcnt) or from registers written long before, the first k-step takes a
+// literal zero accumulator, and the chain ends with mfma_drain before
+// anything reads its result (the count the compiler inserts after this MFMA
+// before a dependent read on gfx950).  The scores use one set of registers:
+// a step's QK chain starts after its softmax has consumed S(t), so S(t+1)
+// takes S(t)'s registers and no copy separates the chain from its readers;
+// tests/test_isa_hazards_cpu.py checks the compiled code for any read of a
+// chain's result, or write of its sources, inside the wait states.
+__device__ __forceinline__ f32x16 mfma_qk_first(const bf16x8& a, const bf16x8& b) {
+  f32x16 d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ void mfma_qk(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_drain(f32x16& d) {
+  asm volatile("s_nop 11" : "+v"(d));
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool OUT_BF16, bool PAGE16>
+__global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
+  constexpr int D = 512;
+  constexpr int KT = 32;            // keys per tile
+  constexpr int NCH = D / 8;        // 16-byte chunks per K row (64)
+  constexpr int KS = D / 16;        // QK k-steps (32)
+  constexpr int DB = D / 32;        // O^T 32-dim blocks (16)
+  constexpr int NT = KT / 16;       // PV k-steps per tile (2)
+  constexpr int NV = NT * DB;       // PV MFMAs per tile (32)
+  constexpr int TILE = KT * D * 2;  // 32 KiB
+  constexpr int AH = 3;             // LDS operand reads in flight ahead of the MFMAs
+  constexpr int NWAVE = 4;
+  // O and the row sums are rescaled only when a row's maximum rises by more
+  // than kSlack (log2 units) over the one they are scaled to: P stays below
+  // 2^16 and the rescale (256 accumulators) is rare.
+  constexpr float kSlack = 16.0f;
+
+  __shared__ __attribute__((aligned(1024))) char kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb1[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb2[TILE];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int hkv = P.num_kv_heads;
+  const int item = blockIdx.x / hkv;
+  const int kvh = blockIdx.x - item * hkv;
+  const int b = ldu(P.items + 4 * item + 0);
+  const int t0 = ldu(P.items + 4 * item + 1);
+  const int k_lo = ldu(P.items + 4 * item + 2);
+  const int k_hi = ldu(P.items + 4 * item + 3);
+  const int q_beg = ldu(P.qo_indptr + b);
+  const int qo_len = ldu(P.qo_indptr + b + 1) - q_beg;
+  const int kvl = ldu(P.kv_len + b);
+  const int start = kvl - qo_len;
+  const int pg0 = ldu(P.kv_page_indptr + b);
+  const int32_t* pages = P.kv_page_indices + pg0;
+  const int last_page = ldu(P.kv_page_indptr + b + 1) - pg0 - 1;
+  const int gs = P.group_shift;
+  const int tok_w = 32 >> gs;  // tokens per wave
+  const int wl = P.window_left;
+
+  // this lane's query row: token t0 + tl, head kvh * group + hh
+  const int tl = w * tok_w + (n >> gs);
+  const int hh = n & ((1 << gs) - 1);
+  const int tok = t0 + tl;
+  const bool row_valid = tok < qo_len;
+  const int pos = start + tok;
+  const int head = (kvh << gs) + hh;
+  const int hi_n = row_valid ? min(k_hi, pos) : -1;
+  const int lo_n = max(k_lo, wl >= 0 ? pos - wl : 0);
+  const int wt0 = t0 + w * tok_w;
+  const int w_pmin = start + wt0;
+  const int w_pmax = start + min(wt0 + tok_w, qo_len) - 1;
+  const bool wave_live = wt0 < qo_len;
+
+  const char* kbase_g =
+      reinterpret_cast<const char*>(P.pool + P.layer_off + (int64_t)kvh * P.ps.head);
+  const char* vbase_g = kbase_g + P.ps.kv * 2;
+  const int pshift = PAGE16 ? 4 : P.ps.page_shift;
+  const int psize = PAGE16 ? 16 : P.ps.page_size;
+  const int64_t page_bytes = P.ps.page * 2;
+  const uint32_t pb32 = (uint32_t)page_bytes;  // one page is below 4 GiB (host check)
+  const int jt0 = k_lo / KT;
+  const int ntiles = k_hi / KT - jt0 + 1;
+  const PageRing ring = page_ring(last_page + 1, kvl, pshift);
+
+  // ---- Q of this lane's row, B operands of the QK MFMAs ----
+  // lane (n, h), k-step ks: dims 16 ks + 8 h .. + 7 of row n
+  bf16x8 qf[KS];
+  {
+    const __bf16* qrow = P.q + ((int64_t)(q_beg + (row_valid ? tok : 0)) * P.num_qo_heads + head) * D +
+                         8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
+      qf[ks] = row_valid ? v : bf16x8{};
+    }
+  }
+
+  // ---- tile loads (16 instructions of 1 KiB per K or V^T tile) ----
+  // K: instruction r of wave w loads key 4 r + w, the 64 chunks of its row,
+  // lane l reading chunk l ^ kswz(key) so that LDS position l holds it.
+  // V^T: instruction i = 4 r + w loads chunks (k8 = i / 8, d = 64 (i % 8) + lane),
+  // the 8 keys 8 k8 .. 8 k8 + 7 of dim d.
+  // 16-slot pages: a tile is two pages, kp[0..1] / vp[0..1] their byte offsets.
+  // Lane offsets are formed from an opaque copy of the lane index where they
+  // are used: kept in registers across the loop they would be 16 more VGPRs.
+  // 16-slot pages: the key's row offset goes into the scalar base, the lane
+  // keeps only its chunk offset (lane ^ swizzle) * 16; V^T chunks of one dim
+  // are 32 bytes apart, the rest of the address is scalar.
+  auto k_load = [&](char* kl, int j0, const uint64_t* kp, int r) __attribute__((always_inline)) {
+    const int key = 4 * r + w;  // r < 4: first page of the tile
+    const uint32_t chunk = (uint32_t)((opaque(lane) ^ kswz(key)) << 4);
+    if constexpr (PAGE16) {
+      lds_dma16_s(kbase_g + kp[r >> 2] + (uint32_t)((4 * (r & 3) + w) * (D * 2)), chunk,
+                  kl + key * 1024);
+    } else {
+      const int jj = j0 + key;
+      const int64_t pg = ldu(pages + ring(jj >> pshift));
+      lds_dma16(kbase_g + pg * page_bytes + (int64_t)(jj & (psize - 1)) * (D * 2) + chunk,
+                kl + key * 1024);
+    }
+  };
+  auto v_load = [&](char* vl, int j0, const uint64_t* vp, int r) __attribute__((always_inline)) {
+    const int ins = 4 * r + w;
+    const int k8 = r >> 1;                       // = ins / 8, as w < 4
+    const int d0 = 64 * (4 * (r & 1) + w);       // = 64 (ins % 8)
+    if constexpr (PAGE16) {
+      lds_dma16_s(vbase_g + vp[k8 >> 1] + (uint32_t)(d0 * 32 + 16 * (k8 & 1)),
+                  (uint32_t)opaque(lane) * 32, vl + ins * 1024);
+    } else {
+      const int d = d0 + lane;
+      const int jj = j0 + 8 * k8;
+      const int64_t pg = ldu(pages + ring(jj >> pshift));
+      lds_dma16(vbase_g + pg * page_bytes + (int64_t)d * psize * 2 + (jj & (psize - 1)) * 2,
+                vl + ins * 1024);
+    }
+  };
+  // Zero, in the V^T chunks this wave loaded, the keys at or past kv_len (their
+  // pool slots may hold anything, NaN included, and 0 * NaN would reach O).
+  auto v_sanitize = [&](char* vl, int j0) __attribute__((always_inline)) {
+    if (j0 + KT <= kvl) return;
+    rare_path();
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int ins = 4 * r + w;
+      const int jc = j0 + 8 * (ins >> 3);
+      if (jc + 8 > kvl) {
+        bf16x8* cp = reinterpret_cast<bf16x8*>(vl + ins * 1024 + lane * 16);
+        bf16x8 v = *cp;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (jc + e >= kvl) ? (__bf16)0.0f : v[e];
+        *cp = v;
+      }
+    }
+  };
+  // Page byte offsets of tiles (16-slot pages): lanes 0-1 hold the two pages
+  // of one tile, lanes 2-3 those of another, fetched with one vector load a
+  // step before they are used and read back with readlane.
+  auto fetch_pids = [&](int tile_a, int tile_b) __attribute__((always_inline)) {
+    int r = 0;
+    if (lane < 4) {
+      const int jt = jt0 + (lane < 2 ? tile_a : tile_b);
+      r = pages[ring(2 * jt + (lane & 1))];
+    }
+    return r;
+  };
+  auto settled = [](int v) {
+    int r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+  };
+  // page byte offset from a page id: 64-bit (a pool may pass 4 GiB)
+  auto pid_off = [&](int pid, int l) __attribute__((always_inline)) {
+    return (uint64_t)(uint32_t)__builtin_amdgcn_readlane(pid, l) * pb32;
+  };
+
+  // ---- LDS operand addresses ----
+  const int krow = kperm(n);
+  const int ksw = kswz(krow);
+  const int kaddr0 = krow * NCH * 16 + 16 * (h ^ (ksw & 1)) + 32 * (ksw >> 1);
+  const int vaddr0 = (h * D + n) * 16;
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+  float m_run = kNegBig;
+  float l_run = 0.0f;
+  const float c2 = P.scale_log2;
+  f32x16 s = {};      // S(t): scores whose softmax runs in the current step
+  bf16x8 pb[NT];      // P(t-1), the B operands of the current step's PV
+#pragma unroll
+  for (int t = 0; t < NT; ++t) pb[t] = bf16x8{};
+  bf16x8 ra[AH + 1];  // A operands: V^T chunks (PV ops), then K chunks (QK ops)
+
+  // Tiles inside every row's keys (no element mask): starts in [full_lo, full_hi].
+  const int full_lo = wave_live ? max(k_lo, wl >= 0 ? w_pmax - wl : k_lo) : 0x7fffffff;
+  const int full_hi = min(k_hi, w_pmin) - (KT - 1);
+
+  // operand read of op i of a step (PV ops first when the step has them)
+  // ka, va: opaque copies of kaddr0, vaddr0 made once per step, so that the
+  // compiler forms each op's address from them instead of holding 64
+  // precomputed addresses in registers across the loop
+  auto load_op = [&](int i, auto pv_c, const char* vl, const char* kl, int ka, int va)
+                     __attribute__((always_inline)) {
+    constexpr bool PV = decltype(pv_c)::value;
+    if (PV && i < NV) {
+      const int db = i / NT, t = i % NT;  // O block db takes its NT MFMAs back to back
+      ra[i % (AH + 1)] = *reinterpret_cast<const bf16x8*>(vl + va + (2 * t * D + 32 * db) * 16);
+    } else {
+      const int ks = PV ? i - NV : i;
+      ra[i % (AH + 1)] =
+          *reinterpret_cast<const bf16x8*>(kl + (ka ^ ((ks & 7) << 5)) + (ks >> 3) * 256);
+    }
+  };
+
+  // K buffer roles: Kr holds K(t+1) (read by this step's QK), Kw the buffer
+  // K(t+2) is loaded into.  V buffer roles: Vp holds V(t-1) (read by this
+  // step's PV), Vc holds V(t) (read by the next step), Vn receives V(t+1).
+  char* Kr = kb1;
+  char* Kw = kb0;
+  char* Vp = vb2;
+  char* Vc = vb0;
+  char* Vn = vb1;
+  int pid = 0;        // page ids of this step's loads (16-slot pages)
+
+  // ---- prologue: K(0), K(1), V(0) resident, S(0) = K(0) Q^T ----
+  {
+    const int j0 = jt0 * KT;
+    uint64_t p0[2] = {0, 0}, p1[2] = {0, 0};
+    if constexpr (PAGE16) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        p0[p] = (uint64_t)(uint32_t)ldu(pages + ring(2 * jt0 + p)) * pb32;
+        p1[p] = (uint64_t)(uint32_t)ldu(pages + ring(2 * (jt0 + 1) + p)) * pb32;
+      }
+      pid = fetch_pids(2, 1);  // step 0 loads K(2) (lanes 0-1) and V(1) (lanes 2-3)
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) k_load(kb0, j0, p0, r);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) v_load(vb0, j0, p0, r);
+    if (ntiles > 1) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) k_load(kb1, j0 + KT, p1, r);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    v_sanitize(vb0, j0);
+    lds_barrier();
+    if constexpr (PAGE16) pid = settled(pid);
+    const int ka = kaddr0;
+#pragma unroll
+    for (int i = 0; i < AH; ++i) load_op(i, std::false_type{}, nullptr, kb0, ka, 0);
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      if (i + AH < KS) load_op(i + AH, std::false_type{}, nullptr, kb0, ka, 0);
+      if (i == 0) s = mfma_qk_first(ra[0], qf[0]);
+      else mfma_qk(s, ra[i % (AH + 1)], qf[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mfma_drain(s);
+    // every wave is done with K(0) before step 0 loads K(2) over it
+    lds_barrier();
+  }
+
+  // One step t.  PV: O += P(t-1) V(t-1); QK: S(t+1) = K(t+1) Q^T; SM: the
+  // softmax of S(t); LK / LV: loads of K(t+2) / V(t+1).  The flags are
+  // compile-time so that no MFMA or load of a step sits behind a branch.
+  auto step = [&](int t, auto pv_c, auto qk_c, auto sm_c, auto lk_c, auto lv_c)
+                  __attribute__((always_inline)) {
+    constexpr bool PV = decltype(pv_c)::value, QK = decltype(qk_c)::value;
+    constexpr bool SM = decltype(sm_c)::value;
+    constexpr bool LK = decltype(lk_c)::value, LV = decltype(lv_c)::value;
+    constexpr int NOP = (PV ? NV : 0) + (QK ? KS : 0);
+    const int j0 = (jt0 + t) * KT;  // first key of tile t
+    // page ids of the next step's loads: K(t+3) (lanes 0-1), V(t+2) (lanes 2-3)
+    int pid_next = 0;
+    if constexpr (PAGE16) {
+      if (LK || LV) pid_next = fetch_pids(t + 3, t + 2);
+    }
+    uint64_t kp[2] = {0, 0}, vp[2] = {0, 0};
+    if constexpr (PAGE16) {
+      if (LK) { kp[0] = pid_off(pid, 0); kp[1] = pid_off(pid, 1); }
+      if (LV) { vp[0] = pid_off(pid, 2); vp[1] = pid_off(pid, 3); }
+    }
+    // masked tiles (and a negative scale) scale and mask the scores up
+    // front; the exponentials below then use them as they are
+    bool plain = true;
+    if (SM) {
+      plain = j0 >= full_lo && j0 <= full_hi && c2 >= 0.0f;
+      if (!plain) {
+        rare_path();
+        // register r holds key j0 + 16 (r / 8) + 8 h + r % 8
+        const int kb0_ = j0 + 8 * h - lo_n;
+        const unsigned span = (unsigned)(hi_n - lo_n);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const unsigned rel = (unsigned)(kb0_ + 16 * (r >> 3) + (r & 7));
+          s[r] = rel <= span ? s[r] * c2 : -__builtin_inff();
+        }
+      }
+    }
+    const float cmul = plain ? c2 : 1.0f;
+    float mx = -__builtin_inff(), m_use = m_run, m_new = m_run;
+    bool need = false;
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    uint32_t pnu[8];    // P(t) as bf16 pairs (keys 2j, 2j + 1 of the lane)
+    const int ka = opaque(kaddr0), va = opaque(vaddr0);
+    // the preloaded operands and P pass through an empty statement that stays
+    // after the barrier, so no MFMA of the step is hoisted above it
+#pragma unroll
+    for (int i = 0; i < AH; ++i) asm volatile("" : "+v"(ra[i]));
+    if (PV) asm volatile("" : "+v"(pb[0]), "+v"(pb[1]));
+    if (!PV) {
+#pragma unroll
+      for (int i = 0; i < AH; ++i) load_op(i, std::false_type{}, Vp, Kr, ka, va);
+    }
+    // softmax schedule over the ops: max at ops 1-4, reduction at op 5, the
+    // 16 exponentials at ops 6-21, all inside the PV half when the step has
+    // one (the QK half spends its spare issue cycles on the MFMAs' wait
+    // states); parts a short step has no op for run after its MFMAs
+    constexpr int ESTEP = 1;
+    constexpr int SM_END = 6 + 16 * ESTEP;
+    auto sm_at = [&](int i) __attribute__((always_inline)) {
+      if (i >= 1 && i <= 4) {
+#pragma unroll
+        for (int r = 4 * (i - 1); r < 4 * i; ++r) mx = fmaxf(mx, s[r]);
+      }
+      if (i == 5) {
+        mx = max_with_partner_half(mx * cmul);
+        m_new = fmaxf(m_run, mx);
+        need = __any(m_new > m_run + kSlack);
+        m_use = need ? m_new : m_run;
+      }
+      if (i >= 6 && (i - 6) % ESTEP == 0 && (i - 6) / ESTEP < 16) {
+        // P(t) in place of S(t); every second exponential rounds the pair to
+        // bf16 (the PV operand) and adds the rounded values to the row sum,
+        // so that O is normalised by the sum of the weights it was built
+        // from (a row dominated by one key then returns that key's V as it
+        // is, instead of off by the key's rounding)
+        const int e = (i - 6) / ESTEP;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], cmul, -m_use));
+        s[e] = p;
+        if (e & 1) {
+          const bf16x2 pk = {(__bf16)s[e - 1], (__bf16)p};
+          const uint32_t u = __builtin_bit_cast(uint32_t, pk);
+          ls[(e >> 1) & 3] += __builtin_bit_cast(float, u << 16) +
+                              __builtin_bit_cast(float, u & 0xffff0000u);
+          pnu[e >> 1] = u;
+          pin(__builtin_bit_cast(float, u));
+        }
+      }
+    };
+    // a step without PV (the first) writes S(t+1) over S(t) from its first
+    // op: its softmax runs before the MFMAs
+    if (SM && !PV) {
+#pragma unroll
+      for (int i = 0; i < SM_END; ++i) sm_at(i);
+    }
+#pragma unroll
+    for (int i = 0; i < NOP; ++i) {
+      if (i + AH < NOP) load_op(i + AH, pv_c, Vp, Kr, ka, va);
+      if (PV && i < NV) {
+        oacc[i / NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[i % (AH + 1)], pb[i % NT],
+                                                                oacc[i / NT], 0, 0, 0);
+      } else {
+        // S(t+1) into the registers of S(t), whose softmax is complete
+        const int ks = PV ? i - NV : i;
+        if (ks == 0) s = mfma_qk_first(ra[i % (AH + 1)], qf[0]);
+        else mfma_qk(s, ra[i % (AH + 1)], qf[ks]);
+      }
+      // loads: V(t+1) at even ops 0..14, K(t+2) at even ops 16..30
+      if (LV && i % 2 == 0 && i < 16) v_load(Vn, j0 + KT, vp, i / 2);
+      if (LK && i % 2 == 0 && i >= 16 && i < 32) k_load(Kw, j0 + 2 * KT, kp, (i - 16) / 2);
+      if (SM && PV) sm_at(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    static_assert(!PV || NV >= SM_END, "the softmax fits in the PV half");
+    // loads a step too short to carry them (every step with loads has 32 ops
+    // or more: no such case today)
+    static_assert(!(LV || LK) || NOP >= 32, "a step with loads has at least 32 ops");
+    // the loads of this step landed: publish V(t+1) (zeroed past kv_len) and K(t+2)
+    __builtin_amdgcn_s_waitcnt(0);
+    if (LV) v_sanitize(Vn, j0 + KT);
+    if (SM) {
+      if (need) {
+        rare_path();
+        // O was accumulated against m_run (the last PV of it issued at the
+        // start of this step); nothing to rescale before the first tile
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        if (m_run > 0.5f * kNegBig) {
+          // one block at a time: read into VGPRs, scale, write back (the
+          // scheduler would otherwise read all 256 accumulators first)
+#pragma unroll
+          for (int i = 0; i < DB; ++i) {
+            // pinned to the accumulator registers on both sides, so that the
+            // block is scaled in place (otherwise the allocator moves all
+            // 256 accumulators around the branch)
+            asm volatile("" : "+a"(oacc[i]));
+            f32x16 t = oacc[i];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) t[e] *= alpha;
+            oacc[i] = t;
+            asm volatile("" : "+a"(oacc[i]));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    }
+    if constexpr (PAGE16) {
+      if (LK || LV) pid = settled(pid_next);
+    }
+    if (SM) {
+      // P(t), the B operands of the next step's PV (register r of half h:
+      // key 16 (r / 8) + 8 h + r % 8)
+#pragma unroll
+      for (int q = 0; q < NT; ++q) {
+        const u32x4 v = {pnu[4 * q], pnu[4 * q + 1], pnu[4 * q + 2], pnu[4 * q + 3]};
+        pb[q] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+    // first operands of the next step's PV: V(t), published a step ago
+    if (SM) {
+      const int va2 = opaque(vaddr0);
+#pragma unroll
+      for (int i = 0; i < AH; ++i) load_op(i, std::true_type{}, Vc, Kw, 0, va2);
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc37f);  // lgkmcnt(3): all but the three operand reads
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (QK) mfma_drain(s);  // S(t+1) complete before anything reads it
+    char* const kt = Kr;
+    Kr = Kw;
+    Kw = kt;
+    char* const vt = Vp;
+    Vp = Vc;
+    Vc = Vn;
+    Vn = vt;
+  };
+
+  using T = std::true_type;
+  using F = std::false_type;
+  // step 0 (no PV), then full steps, then the last two tile steps and the
+  // final PV
+  if (ntiles >= 3) step(0, F{}, T{}, T{}, T{}, T{});
+  else if (ntiles == 2) step(0, F{}, T{}, T{}, F{}, T{});
+  else step(0, F{}, F{}, T{}, F{}, F{});
+  int t = 1;
+  for (; t + 2 < ntiles; ++t) step(t, T{}, T{}, T{}, T{}, T{});
+  if (t + 1 < ntiles) {  // t == ntiles - 2 >= 1
+    step(t, T{}, T{}, T{}, F{}, T{});
+    ++t;
+  }
+  if (t < ntiles) {      // t == ntiles - 1 >= 1
+    step(t, T{}, F{}, T{}, F{}, F{});
+    ++t;
+  }
+  step(t, T{}, F{}, F{}, F{}, F{});  // PV(ntiles - 1)
+
+  // every wave is done reading its last tiles: LDS is free
+  __builtin_amdgcn_s_waitcnt(0);
+  lds_barrier();
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.0f / l_tot;
+  // lane (n, h), O^T block db, register r holds dim 32 db + 8 (r / 4) + 4 h + r % 4
+  if constexpr (OUT_BF16) {
+    // O rows of this wave through 32 KiB of LDS: [row n][64 chunks of 16 B],
+    // chunk c of row n at position c ^ n; then one whole row per store
+    char* const stg = w == 0 ? kb0 : w == 1 ? kb1 : w == 2 ? vb0 : vb1;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v = {(__bf16)(oacc[db][4 * g] * inv), (__bf16)(oacc[db][4 * g + 1] * inv),
+                    (__bf16)(oacc[db][4 * g + 2] * inv), (__bf16)(oacc[db][4 * g + 3] * inv)};
+        *reinterpret_cast<bf16x4*>(stg + n * 1024 + (((4 * db + g) ^ n) << 4) + 8 * h) = v;
+      }
+    // LDS operations of one wave complete in order: no wait between the
+    // writes above and the reads below, only no compiler reordering
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll 4
+    for (int r = 0; r < 32; ++r) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(stg + r * 1024 + ((lane ^ r) << 4));
+      const int tt = t0 + w * tok_w + (r >> gs);
+      if (tt < qo_len) {
+        const int hd = (kvh << gs) + (r & ((1 << gs) - 1));
+        *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(P.o) +
+                                   ((int64_t)(q_beg + tt) * P.num_qo_heads + hd) * D + lane * 8) = v;
+      }
+    }
+  } else {
+    if (!row_valid) return;
+    const int64_t orow = ((int64_t)(q_beg + tok) * P.num_qo_heads + head) * D + 4 * h;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int off = 32 * db + 8 * g;
+        f32x4 v = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
+                   oacc[db][4 * g + 3] * inv};
+        *reinterpret_cast<f32x4*>(static_cast<float*>(P.o) + orow + off) = v;
+      }
+  }
+}
+
+}  // namespace
+}  // namespace psw_dev

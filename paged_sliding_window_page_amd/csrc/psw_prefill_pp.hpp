@@ -35,14 +35,6 @@
 namespace psw_dev {
 namespace {
 
-// A copy of v the compiler cannot see through (values derived from it are
-// recomputed where they are used instead of being held in registers).
-__device__ __forceinline__ int opaque(int v) {
-  int r;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
-  return r;
-}
-
 template <bool OUT_BF16, bool PAGE16>
 __global__ __launch_bounds__(512, 1) void prefill256_pp_kernel(AttnParams P) {
   constexpr int D = 256;

@@ -118,7 +118,7 @@ def test_kv_len_past_i32_fails():
 
 def test_tile_query_checks_in_i32_domain():
     assert psw.prefill_tile_q(2, 256) == 128
-    assert psw.prefill_tile_q(16, 512) == 4
+    assert psw.prefill_tile_q(16, 512) == 8     # 128 rows: 8 tokens x 16 heads
     assert psw.prefill_tile_q(1, 256) == 256
     assert _code(lambda: psw.prefill_tile_q(2 ** 32 + 2, 256)) == "PSW_E_OVERFLOW"
     assert _code(lambda: psw.prefill_tile_q(0, 256)) == "PSW_E_HEADS"

@@ -289,3 +289,24 @@ def test_pool_past_2gib_uses_64bit_offsets():
     say("[gpu] 2 GiB pool case")
     gpu = run_attention(big, window_left=1023, pool=pool, label="2GiB")
     check_close(gpu, oracle_attention(small, window_left=1023), ">2GiB pool")
+
+
+def test_hd512_pool_past_4gib_uses_64bit_page_offsets():
+    """hd512 prefill reading pages past the 4 GiB mark of a 4.6 GB pool (page
+    byte offsets are page id x 32 KiB: past 2^32 from page 131072 on)."""
+    num_pages = 140000
+    small = _global_case(45, [70, 5], [150, 90], num_pages=20)
+    used = small.table.kv_page_indices
+    high = (num_pages - 20 + used).astype(np.int32)        # all above page 131072
+    dev = torch.device("cuda", 0)
+    per_page = 2 * 1 * 16 * 512
+    pool = torch.zeros(num_pages * per_page, dtype=torch.bfloat16, device=dev)
+    pool.view(num_pages, per_page)[num_pages - 20:] = small.pool.view(20, per_page).to(dev)
+    big = synth.AttentionCase(16, 1, 512, 16, num_pages, 1, 0, small.qo_lens, small.kv_lens,
+                              small.qo_indptr,
+                              synth.PageTable(small.table.kv_page_indptr, high,
+                                              small.table.kv_last_page_len),
+                              small.q, pool)
+    say("[gpu] 4 GiB hd512 pool case")
+    gpu = run_attention(big, pool=pool, label="4GiB hd512")
+    check_close(gpu, oracle_attention(small), ">4GiB hd512 pool")
