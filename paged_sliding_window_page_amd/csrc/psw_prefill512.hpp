@@ -43,13 +43,11 @@ namespace {
 // the hardware's wait states itself: a dependent accumulation into the same
 // registers needs none, the chain's sources come from LDS reads (ordered by
 // lgkmcnt) or from registers written long before, the first k-step takes a
-// literal zero accumulator, and the chain ends with mfma_drain before
-// anything reads its result (the count the compiler inserts after this MFMA
-// before a dependent read on gfx950).  The scores use one set of registers:
-// a step's QK chain starts after its softmax has consumed S(t), so S(t+1)
-// takes S(t)'s registers and no copy separates the chain from its readers;
-// tests/test_isa_hazards_cpu.py checks the compiled code for any read of a
-// chain's result, or write of its sources, inside the wait states.
+// literal zero accumulator, and the chain's last MFMA carries the wait states
+// before anything may read its result (the count the compiler inserts after
+// this MFMA before a dependent read on gfx950).  tests/test_isa_hazards_cpu.py
+// checks the compiled code for any read of a chain's result, or write of its
+// sources, inside the wait states.
 __device__ __forceinline__ f32x16 mfma_qk_first(const bf16x8& a, const bf16x8& b) {
   f32x16 d;
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
@@ -58,11 +56,22 @@ __device__ __forceinline__ f32x16 mfma_qk_first(const bf16x8& a, const bf16x8& b
 __device__ __forceinline__ void mfma_qk(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void mfma_drain(f32x16& d) {
-  asm volatile("s_nop 11" : "+v"(d));
+// The chain's last MFMA, followed by the wait states in the same statement, so
+// that even a register copy the compiler places right after it is safe.
+__device__ __forceinline__ void mfma_qk_last(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 11" : "+v"(d) : "v"(a), "v"(b));
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// v_max3_f32 as one instruction: fmaxf on values the compiler cannot prove
+// canonical costs two extra quieting instructions per operand.  The scores
+// are finite or -inf here, never NaN.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <bool OUT_BF16, bool PAGE16>
@@ -149,70 +158,37 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
   }
 
   // ---- tile loads (16 instructions of 1 KiB per K or V^T tile) ----
-  // K: instruction r of wave w loads key 4 r + w, the 64 chunks of its row,
-  // lane l reading chunk l ^ kswz(key) so that LDS position l holds it.
-  // V^T: instruction i = 4 r + w loads chunks (k8 = i / 8, d = 64 (i % 8) + lane),
-  // the 8 keys 8 k8 .. 8 k8 + 7 of dim d.
-  // 16-slot pages: a tile is two pages, kp[0..1] / vp[0..1] their byte offsets.
-  // Lane offsets are formed from an opaque copy of the lane index where they
-  // are used: kept in registers across the loop they would be 16 more VGPRs.
-  // 16-slot pages: the key's row offset goes into the scalar base, the lane
-  // keeps only its chunk offset (lane ^ swizzle) * 16; V^T chunks of one dim
-  // are 32 bytes apart, the rest of the address is scalar.
-  auto k_load = [&](char* kl, int j0, const uint64_t* kp, int r) __attribute__((always_inline)) {
-    const int key = 4 * r + w;  // r < 4: first page of the tile
-    const uint32_t chunk = (uint32_t)((opaque(lane) ^ kswz(key)) << 4);
-    if constexpr (PAGE16) {
-      lds_dma16_s(kbase_g + kp[r >> 2] + (uint32_t)((4 * (r & 3) + w) * (D * 2)), chunk,
-                  kl + key * 1024);
-    } else {
-      const int jj = j0 + key;
-      const int64_t pg = ldu(pages + ring(jj >> pshift));
-      lds_dma16(kbase_g + pg * page_bytes + (int64_t)(jj & (psize - 1)) * (D * 2) + chunk,
-                kl + key * 1024);
-    }
-  };
-  auto v_load = [&](char* vl, int j0, const uint64_t* vp, int r) __attribute__((always_inline)) {
-    const int ins = 4 * r + w;
-    const int k8 = r >> 1;                       // = ins / 8, as w < 4
-    const int d0 = 64 * (4 * (r & 1) + w);       // = 64 (ins % 8)
-    if constexpr (PAGE16) {
-      lds_dma16_s(vbase_g + vp[k8 >> 1] + (uint32_t)(d0 * 32 + 16 * (k8 & 1)),
-                  (uint32_t)opaque(lane) * 32, vl + ins * 1024);
-    } else {
-      const int d = d0 + lane;
-      const int jj = j0 + 8 * k8;
-      const int64_t pg = ldu(pages + ring(jj >> pshift));
-      lds_dma16(vbase_g + pg * page_bytes + (int64_t)d * psize * 2 + (jj & (psize - 1)) * 2,
-                vl + ins * 1024);
-    }
-  };
-  // Zero, in the V^T chunks this wave loaded, the keys at or past kv_len (their
-  // pool slots may hold anything, NaN included, and 0 * NaN would reach O).
-  auto v_sanitize = [&](char* vl, int j0) __attribute__((always_inline)) {
-    if (j0 + KT <= kvl) return;
-    rare_path();
+  // K: wave w loads keys 4 w .. 4 w + 3 of each of the tile's two 16-key
+  // halves, one 1 KiB row per instruction, lane l reading chunk l ^ kswz(key)
+  // so that LDS position l holds it.  The four rows of a half lie in one page
+  // (pages hold at least 8 keys) in consecutive slots and in consecutive LDS
+  // rows, so they share one scalar base and one M0 and step by the
+  // instruction offset, which the load applies to both addresses.  V^T:
+  // wave w loads the chunks of k8 = w (keys 8 w .. 8 w + 7, one page) for
+  // dims 64 j .. 64 j + 63, j < 8: one scalar base, the lane's offset
+  // 2 P (64 j + lane) held in a register.  So each wave needs three page ids
+  // per tile step (its two K halves, its V keys), fetched with one vector
+  // load a step ahead (lanes 0-2) and read back with readlane.
+  // kvo[j]: the K lanes' chunk offsets (the swizzle depends on the key only
+  // through w and j); vvo[j]: the V lanes' offsets.  Loop-invariant.
+  uint32_t kvo[4], vvo[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int ins = 4 * r + w;
-      const int jc = j0 + 8 * (ins >> 3);
-      if (jc + 8 > kvl) {
-        bf16x8* cp = reinterpret_cast<bf16x8*>(vl + ins * 1024 + lane * 16);
-        bf16x8 v = *cp;
+  for (int j = 0; j < 4; ++j) kvo[j] = (uint32_t)((lane ^ kswz(4 * w + j)) << 4);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (jc + e >= kvl) ? (__bf16)0.0f : v[e];
-        *cp = v;
-      }
-    }
-  };
-  // Page byte offsets of tiles (16-slot pages): lanes 0-1 hold the two pages
-  // of one tile, lanes 2-3 those of another, fetched with one vector load a
-  // step before they are used and read back with readlane.
-  auto fetch_pids = [&](int tile_a, int tile_b) __attribute__((always_inline)) {
+  for (int j = 0; j < 8; ++j) vvo[j] = (uint32_t)((64 * j + lane) * 2 * psize);
+  // the keys whose pages a wave loads for a tile starting at key j0
+  auto k_key = [&](int j0, int half) __attribute__((always_inline)) { return j0 + 16 * half + 4 * w; };
+  auto v_key = [&](int j0) __attribute__((always_inline)) { return j0 + 8 * w; };
+  // page id of a key (keys past the request's pages read a resident page;
+  // they are masked and their V zeroed)
+  auto page_of = [&](int key) __attribute__((always_inline)) { return pages[ring(key >> pshift)]; };
+  // lanes 0-1: the pages of the K halves of tile tk, lane 2: the page of the
+  // V keys of tile tv
+  auto fetch_pids = [&](int tk, int tv) __attribute__((always_inline)) {
     int r = 0;
-    if (lane < 4) {
-      const int jt = jt0 + (lane < 2 ? tile_a : tile_b);
-      r = pages[ring(2 * jt + (lane & 1))];
+    if (lane < 3) {
+      const int jk = (jt0 + tk) * KT, jv = (jt0 + tv) * KT;
+      r = page_of(lane < 2 ? k_key(jk, lane) : v_key(jv));
     }
     return r;
   };
@@ -221,9 +197,50 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
     asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
     return r;
   };
-  // page byte offset from a page id: 64-bit (a pool may pass 4 GiB)
-  auto pid_off = [&](int pid, int l) __attribute__((always_inline)) {
-    return (uint64_t)(uint32_t)__builtin_amdgcn_readlane(pid, l) * pb32;
+  // byte offset of a page (64-bit: a pool may pass 4 GiB) plus a slot offset
+  auto page_off = [&](int page) __attribute__((always_inline)) {
+    return (uint64_t)(uint32_t)page * pb32;
+  };
+  // byte offsets, inside the pool's K and V blocks, of what a wave loads for
+  // a tile starting at key j0: K halves (first key's row), V (first key's slot)
+  auto k_off = [&](int page, int j0, int half) __attribute__((always_inline)) {
+    return page_off(page) + (uint32_t)((k_key(j0, half) & (psize - 1)) * (D * 2));
+  };
+  auto v_off = [&](int page, int j0) __attribute__((always_inline)) {
+    return page_off(page) + (uint32_t)((v_key(j0) & (psize - 1)) * 2);
+  };
+  auto k_load_half = [&](char* kl, uint64_t koff, int half) __attribute__((always_inline)) {
+    const char* base = kbase_g + koff;
+    const uint32_t m0 =
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(kl + (16 * half + 4 * w) * 1024);
+    asm volatile(
+        "s_mov_b32 m0, %4\n\t"
+        "global_load_lds_dwordx4 %0, %5\n\t"
+        "global_load_lds_dwordx4 %1, %5 offset:1024\n\t"
+        "global_load_lds_dwordx4 %2, %5 offset:2048\n\t"
+        "global_load_lds_dwordx4 %3, %5 offset:3072"
+        :
+        : "v"(kvo[0]), "v"(kvo[1]), "v"(kvo[2]), "v"(kvo[3]), "s"(m0), "s"(base)
+        : "memory", "m0");
+  };
+  auto v_load = [&](char* vl, uint64_t voff, int j) __attribute__((always_inline)) {
+    lds_dma16_s(vbase_g + voff, vvo[j], vl + (8 * w + j) * 1024);
+  };
+  // Zero, in the V^T chunks this wave loaded (keys 8 w .. 8 w + 7), the keys
+  // at or past kv_len (their pool slots may hold anything, NaN included, and
+  // 0 * NaN would reach O).
+  auto v_sanitize = [&](char* vl, int j0) __attribute__((always_inline)) {
+    const int jc = v_key(j0);
+    if (jc + 8 <= kvl) return;
+    rare_path();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bf16x8* cp = reinterpret_cast<bf16x8*>(vl + (8 * w + j) * 1024 + lane * 16);
+      bf16x8 v = *cp;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (jc + e >= kvl) ? (__bf16)0.0f : v[e];
+      *cp = v;
+    }
   };
 
   // ---- LDS operand addresses ----
@@ -238,7 +255,7 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
   float m_run = kNegBig;
   float l_run = 0.0f;
   const float c2 = P.scale_log2;
-  f32x16 s = {};      // S(t): scores whose softmax runs in the current step
+  f32x16 sbuf[2] = {};  // S(t) and S(t+1), alternating by step parity
   bf16x8 pb[NT];      // P(t-1), the B operands of the current step's PV
 #pragma unroll
   for (int t = 0; t < NT; ++t) pb[t] = bf16x8{};
@@ -273,43 +290,40 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
   char* Vp = vb2;
   char* Vc = vb0;
   char* Vn = vb1;
-  int pid = 0;        // page ids of this step's loads (16-slot pages)
+  int pid = 0;        // page ids of this step's loads (lanes 0-2)
 
   // ---- prologue: K(0), K(1), V(0) resident, S(0) = K(0) Q^T ----
   {
     const int j0 = jt0 * KT;
-    uint64_t p0[2] = {0, 0}, p1[2] = {0, 0};
-    if constexpr (PAGE16) {
+    const int pk0 = ldu(pages + ring(k_key(j0, 0) >> pshift));
+    const int pk1 = ldu(pages + ring(k_key(j0, 1) >> pshift));
+    const int pv0 = ldu(pages + ring(v_key(j0) >> pshift));
+    k_load_half(kb0, k_off(pk0, j0, 0), 0);
+    k_load_half(kb0, k_off(pk1, j0, 1), 1);
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        p0[p] = (uint64_t)(uint32_t)ldu(pages + ring(2 * jt0 + p)) * pb32;
-        p1[p] = (uint64_t)(uint32_t)ldu(pages + ring(2 * (jt0 + 1) + p)) * pb32;
-      }
-      pid = fetch_pids(2, 1);  // step 0 loads K(2) (lanes 0-1) and V(1) (lanes 2-3)
-    }
-#pragma unroll
-    for (int r = 0; r < 8; ++r) k_load(kb0, j0, p0, r);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) v_load(vb0, j0, p0, r);
+    for (int j = 0; j < 8; ++j) v_load(vb0, v_off(pv0, j0), j);
     if (ntiles > 1) {
-#pragma unroll
-      for (int r = 0; r < 8; ++r) k_load(kb1, j0 + KT, p1, r);
+      const int pk2 = ldu(pages + ring(k_key(j0 + KT, 0) >> pshift));
+      const int pk3 = ldu(pages + ring(k_key(j0 + KT, 1) >> pshift));
+      k_load_half(kb1, k_off(pk2, j0 + KT, 0), 0);
+      k_load_half(kb1, k_off(pk3, j0 + KT, 1), 1);
     }
+    pid = fetch_pids(2, 1);  // step 0 loads K(2) and V(1)
     __builtin_amdgcn_s_waitcnt(0);
     v_sanitize(vb0, j0);
     lds_barrier();
-    if constexpr (PAGE16) pid = settled(pid);
+    pid = settled(pid);
     const int ka = kaddr0;
 #pragma unroll
     for (int i = 0; i < AH; ++i) load_op(i, std::false_type{}, nullptr, kb0, ka, 0);
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
       if (i + AH < KS) load_op(i + AH, std::false_type{}, nullptr, kb0, ka, 0);
-      if (i == 0) s = mfma_qk_first(ra[0], qf[0]);
-      else mfma_qk(s, ra[i % (AH + 1)], qf[i]);
+      if (i == 0) sbuf[0] = mfma_qk_first(ra[0], qf[0]);
+      else if (i < KS - 1) mfma_qk(sbuf[0], ra[i % (AH + 1)], qf[i]);
+      else mfma_qk_last(sbuf[0], ra[i % (AH + 1)], qf[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    mfma_drain(s);
     // every wave is done with K(0) before step 0 loads K(2) over it
     lds_barrier();
   }
@@ -317,23 +331,32 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
   // One step t.  PV: O += P(t-1) V(t-1); QK: S(t+1) = K(t+1) Q^T; SM: the
   // softmax of S(t); LK / LV: loads of K(t+2) / V(t+1).  The flags are
   // compile-time so that no MFMA or load of a step sits behind a branch.
-  auto step = [&](int t, auto pv_c, auto qk_c, auto sm_c, auto lk_c, auto lv_c)
+  // The scores alternate between two register sets: S(t) is read from
+  // sbuf[PAR] while the QK chain writes S(t+1) into sbuf[PAR ^ 1], so the
+  // softmax spreads over all 64 MFMAs of the step.
+  // PAR 2 + x: "same-set" step on sbuf[x]: S(t+1) overwrites S(t) in the QK
+  // half, so the softmax runs in the PV half (the steps after the pairs).
+  auto step = [&](int t, auto par_c, auto pv_c, auto qk_c, auto sm_c, auto lk_c, auto lv_c)
                   __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par_c)::value & 1;
+    constexpr bool SAME = decltype(par_c)::value >= 2;
     constexpr bool PV = decltype(pv_c)::value, QK = decltype(qk_c)::value;
     constexpr bool SM = decltype(sm_c)::value;
     constexpr bool LK = decltype(lk_c)::value, LV = decltype(lv_c)::value;
     constexpr int NOP = (PV ? NV : 0) + (QK ? KS : 0);
+    static_assert(!SAME || PV || !QK, "a same-set step overwrites S(t) only after its PV half");
+    f32x16& sc = sbuf[PAR];                // S(t)
+    f32x16& sn = sbuf[SAME ? PAR : PAR ^ 1];  // S(t+1)
     const int j0 = (jt0 + t) * KT;  // first key of tile t
-    // page ids of the next step's loads: K(t+3) (lanes 0-1), V(t+2) (lanes 2-3)
+    // page ids of the next step's loads: K(t+3) (lanes 0-1), V(t+2) (lane 2)
     int pid_next = 0;
-    if constexpr (PAGE16) {
-      if (LK || LV) pid_next = fetch_pids(t + 3, t + 2);
+    if (LK || LV) pid_next = fetch_pids(t + 3, t + 2);
+    uint64_t kp[2] = {0, 0}, vp = 0;
+    if (LK) {
+      kp[0] = k_off(__builtin_amdgcn_readlane(pid, 0), j0 + 2 * KT, 0);
+      kp[1] = k_off(__builtin_amdgcn_readlane(pid, 1), j0 + 2 * KT, 1);
     }
-    uint64_t kp[2] = {0, 0}, vp[2] = {0, 0};
-    if constexpr (PAGE16) {
-      if (LK) { kp[0] = pid_off(pid, 0); kp[1] = pid_off(pid, 1); }
-      if (LV) { vp[0] = pid_off(pid, 2); vp[1] = pid_off(pid, 3); }
-    }
+    if (LV) vp = v_off(__builtin_amdgcn_readlane(pid, 2), j0 + KT);
     // masked tiles (and a negative scale) scale and mask the scores up
     // front; the exponentials below then use them as they are
     bool plain = true;
@@ -347,7 +370,7 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const unsigned rel = (unsigned)(kb0_ + 16 * (r >> 3) + (r & 7));
-          s[r] = rel <= span ? s[r] * c2 : -__builtin_inff();
+          sc[r] = rel <= span ? sc[r] * c2 : -__builtin_inff();
         }
       }
     }
@@ -357,57 +380,42 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
     float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     uint32_t pnu[8];    // P(t) as bf16 pairs (keys 2j, 2j + 1 of the lane)
     const int ka = opaque(kaddr0), va = opaque(vaddr0);
-    // the preloaded operands and P pass through an empty statement that stays
-    // after the barrier, so no MFMA of the step is hoisted above it
-#pragma unroll
-    for (int i = 0; i < AH; ++i) asm volatile("" : "+v"(ra[i]));
-    if (PV) asm volatile("" : "+v"(pb[0]), "+v"(pb[1]));
     if (!PV) {
 #pragma unroll
       for (int i = 0; i < AH; ++i) load_op(i, std::false_type{}, Vp, Kr, ka, va);
     }
-    // softmax schedule over the ops: max at ops 1-4, reduction at op 5, the
-    // 16 exponentials at ops 6-21, all inside the PV half when the step has
-    // one (the QK half spends its spare issue cycles on the MFMAs' wait
-    // states); parts a short step has no op for run after its MFMAs
-    constexpr int ESTEP = 1;
-    constexpr int SM_END = 6 + 16 * ESTEP;
+    // softmax schedule over the step's ops: the row max at ops 1-8, its
+    // reduction at op 9, the 16 exponentials from op 10 on, ES ops apart;
+    // parts a short step has no op for run after its MFMAs
+    constexpr int ES = NOP >= 64 && !SAME ? 3 : 1;
+    constexpr int SM_END = 10 + 16 * ES;
+    static_assert(!SAME || !QK || SM_END <= NV, "a same-set step's softmax ends in its PV half");
     auto sm_at = [&](int i) __attribute__((always_inline)) {
-      if (i >= 1 && i <= 4) {
-#pragma unroll
-        for (int r = 4 * (i - 1); r < 4 * i; ++r) mx = fmaxf(mx, s[r]);
-      }
-      if (i == 5) {
+      if (i >= 1 && i <= 8) mx = max3(mx, sc[2 * i - 2], sc[2 * i - 1]);
+      if (i == 9) {
         mx = max_with_partner_half(mx * cmul);
         m_new = fmaxf(m_run, mx);
         need = __any(m_new > m_run + kSlack);
         m_use = need ? m_new : m_run;
       }
-      if (i >= 6 && (i - 6) % ESTEP == 0 && (i - 6) / ESTEP < 16) {
+      if (i >= 10 && (i - 10) % ES == 0 && (i - 10) / ES < 16) {
         // P(t) in place of S(t); every second exponential rounds the pair to
         // bf16 (the PV operand) and adds the rounded values to the row sum,
         // so that O is normalised by the sum of the weights it was built
         // from (a row dominated by one key then returns that key's V as it
         // is, instead of off by the key's rounding)
-        const int e = (i - 6) / ESTEP;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], cmul, -m_use));
-        s[e] = p;
+        const int e = (i - 10) / ES;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], cmul, -m_use));
+        sc[e] = p;
         if (e & 1) {
-          const bf16x2 pk = {(__bf16)s[e - 1], (__bf16)p};
-          const uint32_t u = __builtin_bit_cast(uint32_t, pk);
-          ls[(e >> 1) & 3] += __builtin_bit_cast(float, u << 16) +
-                              __builtin_bit_cast(float, u & 0xffff0000u);
-          pnu[e >> 1] = u;
-          pin(__builtin_bit_cast(float, u));
+          const bf16x2 pk = {(__bf16)sc[e - 1], (__bf16)p};
+          const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+          ls[(e >> 1) & 3] = __builtin_amdgcn_fdot2_f32_bf16(pk, one, ls[(e >> 1) & 3], false);
+          pnu[e >> 1] = __builtin_bit_cast(uint32_t, pk);
+          pin(__builtin_bit_cast(float, pnu[e >> 1]));
         }
       }
     };
-    // a step without PV (the first) writes S(t+1) over S(t) from its first
-    // op: its softmax runs before the MFMAs
-    if (SM && !PV) {
-#pragma unroll
-      for (int i = 0; i < SM_END; ++i) sm_at(i);
-    }
 #pragma unroll
     for (int i = 0; i < NOP; ++i) {
       if (i + AH < NOP) load_op(i + AH, pv_c, Vp, Kr, ka, va);
@@ -415,20 +423,24 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
         oacc[i / NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[i % (AH + 1)], pb[i % NT],
                                                                 oacc[i / NT], 0, 0, 0);
       } else {
-        // S(t+1) into the registers of S(t), whose softmax is complete
         const int ks = PV ? i - NV : i;
-        if (ks == 0) s = mfma_qk_first(ra[i % (AH + 1)], qf[0]);
-        else mfma_qk(s, ra[i % (AH + 1)], qf[ks]);
+        if (ks == 0) sn = mfma_qk_first(ra[i % (AH + 1)], qf[0]);
+        else if (ks < KS - 1) mfma_qk(sn, ra[i % (AH + 1)], qf[ks]);
+        else mfma_qk_last(sn, ra[i % (AH + 1)], qf[ks]);
       }
-      // loads: V(t+1) at even ops 0..14, K(t+2) at even ops 16..30
-      if (LV && i % 2 == 0 && i < 16) v_load(Vn, j0 + KT, vp, i / 2);
-      if (LK && i % 2 == 0 && i >= 16 && i < 32) k_load(Kw, j0 + 2 * KT, kp, (i - 16) / 2);
-      if (SM && PV) sm_at(i);
+      // loads: K(t+2) at ops 0 and 2 of the PV half, V(t+1) at the first
+      // even ops of the QK half (of the PV half in a step without one), so
+      // that the tile writes into LDS split between the halves
+      constexpr int LB = (PV && QK) ? NV : 4;
+      if (LK && (i == 0 || i == 2)) k_load_half(Kw, kp[i == 2], i == 2);
+      if (LV && i >= LB && i <= LB + 14 && i % 2 == 0) v_load(Vn, vp, (i - LB) / 2);
+      if (SM) sm_at(i);
       __builtin_amdgcn_sched_barrier(0);
     }
-    static_assert(!PV || NV >= SM_END, "the softmax fits in the PV half");
-    // loads a step too short to carry them (every step with loads has 32 ops
-    // or more: no such case today)
+    if (SM) {
+#pragma unroll
+      for (int i = NOP; i < SM_END; ++i) sm_at(i);
+    }
     static_assert(!(LV || LK) || NOP >= 32, "a step with loads has at least 32 ops");
     // the loads of this step landed: publish V(t+1) (zeroed past kv_len) and K(t+2)
     __builtin_amdgcn_s_waitcnt(0);
@@ -448,10 +460,10 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
             // block is scaled in place (otherwise the allocator moves all
             // 256 accumulators around the branch)
             asm volatile("" : "+a"(oacc[i]));
-            f32x16 t = oacc[i];
+            f32x16 tt = oacc[i];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) t[e] *= alpha;
-            oacc[i] = t;
+            for (int e = 0; e < 16; ++e) tt[e] *= alpha;
+            oacc[i] = tt;
             asm volatile("" : "+a"(oacc[i]));
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -461,9 +473,7 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
       }
       l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
-    if constexpr (PAGE16) {
-      if (LK || LV) pid = settled(pid_next);
-    }
+    if (LK || LV) pid = settled(pid_next);
     if (SM) {
       // P(t), the B operands of the next step's PV (register r of half h:
       // key 16 (r / 8) + 8 h + r % 8)
@@ -483,7 +493,6 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
     __builtin_amdgcn_s_waitcnt(0xc37f);  // lgkmcnt(3): all but the three operand reads
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (QK) mfma_drain(s);  // S(t+1) complete before anything reads it
     char* const kt = Kr;
     Kr = Kw;
     Kw = kt;
@@ -495,22 +504,33 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
 
   using T = std::true_type;
   using F = std::false_type;
-  // step 0 (no PV), then full steps, then the last two tile steps and the
-  // final PV
-  if (ntiles >= 3) step(0, F{}, T{}, T{}, T{}, T{});
-  else if (ntiles == 2) step(0, F{}, T{}, T{}, F{}, T{});
-  else step(0, F{}, F{}, T{}, F{}, F{});
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using S1 = std::integral_constant<int, 3>;  // same-set steps on sbuf[1]
+  // step 0 (no PV, S(0) in sbuf[0]), then full steps in pairs (S(t) in
+  // sbuf[t % 2]); after the pairs t is odd, S(t) is in sbuf[1], and the
+  // remaining steps keep it there (same-set steps)
+  if (ntiles >= 3) step(0, P0{}, F{}, T{}, T{}, T{}, T{});
+  else if (ntiles == 2) step(0, P0{}, F{}, T{}, T{}, F{}, T{});
+  else step(0, P0{}, F{}, F{}, T{}, F{}, F{});
   int t = 1;
-  for (; t + 2 < ntiles; ++t) step(t, T{}, T{}, T{}, T{}, T{});
+  for (; t + 3 < ntiles; t += 2) {
+    step(t, P1{}, T{}, T{}, T{}, T{}, T{});
+    step(t + 1, P0{}, T{}, T{}, T{}, T{}, T{});
+  }
+  if (t + 2 < ntiles) {  // one more full step
+    step(t, S1{}, T{}, T{}, T{}, T{}, T{});
+    ++t;
+  }
   if (t + 1 < ntiles) {  // t == ntiles - 2 >= 1
-    step(t, T{}, T{}, T{}, F{}, T{});
+    step(t, S1{}, T{}, T{}, T{}, F{}, T{});
     ++t;
   }
   if (t < ntiles) {      // t == ntiles - 1 >= 1
-    step(t, T{}, F{}, T{}, F{}, F{});
+    step(t, S1{}, T{}, F{}, T{}, F{}, F{});
     ++t;
   }
-  step(t, T{}, F{}, F{}, F{}, F{});  // PV(ntiles - 1)
+  step(t, S1{}, T{}, F{}, F{}, F{}, F{});  // PV(ntiles - 1)
 
   // every wave is done reading its last tiles: LDS is free
   __builtin_amdgcn_s_waitcnt(0);
