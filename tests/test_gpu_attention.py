@@ -204,6 +204,15 @@ def test_hd512_page_sizes(page_size):
     check_close(gpu, oracle_attention(case), f"hd512 P={page_size}")
 
 
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (4, 1), (8, 2), (32, 1)])
+def test_hd512_group_sizes(hq, hkv):
+    """GQA groups other than 16 at head_dim 512: a work-group's 128 query rows
+    are 128 / group tokens x the group's heads, 32 / group tokens per wave."""
+    case = _global_case(43, [70, 1, 33], [70, 129, 300], num_qo_heads=hq, num_kv_heads=hkv)
+    gpu = run_attention(case, label=f"hd512 group {hq // hkv}")
+    check_close(gpu, oracle_attention(case), f"hd512 group {hq // hkv}")
+
+
 @pytest.mark.parametrize("page_size", [16, 32])
 def test_hd512_fp32_output(page_size):
     case = _global_case(47, [100, 7], [230, 64], page_size=page_size)

@@ -52,14 +52,16 @@ def test_decode_group_sizes(hq, hkv):
     check_close(gpu, oracle_attention(case, window_left=200), f"decode group {hq // hkv}")
 
 
-@pytest.mark.parametrize("page_size", [8, 32])
-def test_decode_group32_page_sizes(page_size):
+@pytest.mark.parametrize("hd,page_size", [(256, 8), (256, 32), (512, 16), (512, 8)])
+def test_decode_group32_page_sizes(hd, page_size):
     """The group-32 decode (split mode of the attention kernel) at page sizes
-    other than 16."""
-    case = _case(256, 65, [40, 700, 129, 1], num_qo_heads=32, num_kv_heads=1,
+    other than 16, and at head_dim 512 (32 Q heads on one KV head)."""
+    case = _case(hd, 65, [40, 700, 129, 1], num_qo_heads=32, num_kv_heads=1,
                  page_size=page_size)
-    gpu = run_attention(case, window_left=200, label=f"decode group 32 P={page_size}")
-    check_close(gpu, oracle_attention(case, window_left=200), f"decode group 32 P={page_size}")
+    wl = 200 if hd == 256 else -1
+    gpu = run_attention(case, window_left=wl, label=f"decode hd{hd} group 32 P={page_size}")
+    check_close(gpu, oracle_attention(case, window_left=wl),
+                f"decode hd{hd} group 32 P={page_size}")
 
 
 @pytest.mark.parametrize("wl", [-1, 0, 1, 30, 31, 32, 33, 63, 64, 1023, 10 ** 6])
