@@ -102,6 +102,7 @@ struct PrepParams {
   int32_t num_pages;
   int32_t rope_positions;
   float eps;
+  int32_t n_items;  // set by the launchers that pad the grid
 };
 
 constexpr int kPrepItemInts = 6;

@@ -173,23 +173,35 @@ __device__ __forceinline__ void store_v_transposed(const PrepParams& P, const __
 // are resident and their load / compute / store phases overlap.
 constexpr int kPrepHeads256 = 2;
 
+// Work-groups are dispatched to the 8 XCDs in turn (block x to XCD x % 8),
+// each XCD with its own L2.  The prep grids give an item's head groups blocks
+// x that are equal mod 8, so they all run on one XCD and the item's RoPE rows
+// come into that L2 once (-4.5% on the 8192-token hd256 prep): block x is
+// head group (x / 8) % g of item 8 ((x / 8) / g) + x % 8, for g head groups
+// per item and a grid padded to a multiple of 8 items.
+__device__ __forceinline__ void xcd_item_group(int g, int* item, int* group) {
+  const int k = blockIdx.x >> 3;
+  const int r = k / g;
+  *item = 8 * r + (blockIdx.x & 7);
+  *group = k - r * g;
+}
+
 // hd256.  A work-group takes one item and one group of up to kPrepHeads256
-// heads of one row kind: with g = nqg + 2 nkg groups per item, block x is item
-// x / g and group y = x % g, y < nqg -> Q heads, y < nqg + nkg -> K heads,
-// else V heads.  The kinds interleave in dispatch order, so the V
-// work-groups (a transpose through LDS, slower per byte) spread over the
-// launch instead of all running at its end (-9% on 8192 tokens, with the
-// smaller head groups).  Lane group tt (16 lanes) owns token tt of the item
-// and all the group's heads, so the RoPE rows of its position are loaded once,
-// and every input row of the lane group is requested before the first one is
-// used.
+// heads of one row kind; of the g = nqg + 2 nkg groups of an item, group
+// y < nqg -> Q heads, y < nqg + nkg -> K heads, else V heads.  The kinds
+// interleave in dispatch order, so the V work-groups (a transpose through
+// LDS, slower per byte) spread over the launch instead of all running at its
+// end (-9% on 8192 tokens, with the smaller head groups).  Lane group tt (16
+// lanes) owns token tt of the item and all the group's heads, so the RoPE
+// rows of its position are loaded once, and every input row of the lane group
+// is requested before the first one is used.
 __global__ __launch_bounds__(256) void prep_hd256_kernel(PrepParams P) {
   constexpr int D = 256, LPR = 16, HALF = D / 2, HG = kPrepHeads256;
   const int nqg = (P.num_qo_heads + HG - 1) / HG;
   const int nkg = (P.num_kv_heads + HG - 1) / HG;
-  const int ngr = nqg + 2 * nkg;
-  const int itx = blockIdx.x / ngr;
-  const int y = blockIdx.x - itx * ngr;
+  int itx, y;
+  xcd_item_group(nqg + 2 * nkg, &itx, &y);
+  if (itx >= P.n_items) return;
   const Item it = read_item(P.items + kPrepItemInts * itx);
   if (!item_ok(P, it)) return;
   const int kind = y < nqg ? 0 : (y < nqg + nkg ? 1 : 2);
@@ -353,7 +365,10 @@ constexpr int kQHeads = 2;  // 2: 8% faster than 4 on 8192 tokens x 16 heads
 __global__ __launch_bounds__(256) void prep_q_hd512_kernel(PrepParams P) {
   constexpr int D = 512, LPR = 32, HALF = D / 2, NG = 256 / LPR, HG = kQHeads;
   constexpr int TPG = kPrepMaxTokens / NG;  // tokens per lane group
-  const Item it = read_item(P.items + kPrepItemInts * blockIdx.x);
+  int itx, hgi;
+  xcd_item_group((P.num_qo_heads + HG - 1) / HG, &itx, &hgi);
+  if (itx >= P.n_items) return;
+  const Item it = read_item(P.items + kPrepItemInts * itx);
   const bool ok = it.pos0 >= 0 && it.ntok >= 1 && it.ntok <= kPrepMaxTokens &&
                   it.pos0 + it.ntok <= P.rope_positions;
   if (!ok) {
@@ -366,7 +381,7 @@ __global__ __launch_bounds__(256) void prep_q_hd512_kernel(PrepParams P) {
   }
   const int li = threadIdx.x % LPR;
   const int g = threadIdx.x / LPR;
-  const int h0 = HG * blockIdx.y;
+  const int h0 = HG * hgi;
   const int hcount = min(HG, P.num_qo_heads - h0);
   float w1[8], w2[8];
   load8(P.q_w + 8 * li, w1);
@@ -427,8 +442,11 @@ hipError_t launch_prep_hd256(const PrepParams& p, int n_items, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
   const int64_t groups = (p.num_qo_heads + kPrepHeads256 - 1) / kPrepHeads256 +
                          2 * ((p.num_kv_heads + kPrepHeads256 - 1) / kPrepHeads256);
-  if ((int64_t)n_items * groups > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prep_hd256_kernel, dim3((unsigned)(n_items * groups)), dim3(256), 0, s, p);
+  const int64_t blocks = (((int64_t)n_items + 7) / 8) * 8 * groups;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  PrepParams q = p;
+  q.n_items = n_items;
+  hipLaunchKernelGGL(prep_hd256_kernel, dim3((unsigned)blocks), dim3(256), 0, s, q);
   return hipGetLastError();
 }
 
@@ -440,8 +458,12 @@ hipError_t launch_prep_hd512(const PrepParams& p, int n_items, hipStream_t s) {
 
 hipError_t launch_prep_q_hd512(const PrepParams& p, int n_items, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
-  const int groups = (p.num_qo_heads + kQHeads - 1) / kQHeads;
-  hipLaunchKernelGGL(prep_q_hd512_kernel, dim3(n_items, groups), dim3(256), 0, s, p);
+  const int64_t groups = (p.num_qo_heads + kQHeads - 1) / kQHeads;
+  const int64_t blocks = (((int64_t)n_items + 7) / 8) * 8 * groups;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  PrepParams q = p;
+  q.n_items = n_items;
+  hipLaunchKernelGGL(prep_q_hd512_kernel, dim3((unsigned)blocks), dim3(256), 0, s, q);
   return hipGetLastError();
 }
 
