@@ -182,15 +182,11 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
   // page id of a key (keys past the request's pages read a resident page;
   // they are masked and their V zeroed)
   auto page_of = [&](int key) __attribute__((always_inline)) { return pages[ring(key >> pshift)]; };
-  // lanes 0-1: the pages of the K halves of tile tk, lane 2: the page of the
-  // V keys of tile tv
+  // lanes 0-1: the pages of the K halves of tile tk, lanes 2-63: the page of
+  // the V keys of tile tv (one load instruction, no branch)
   auto fetch_pids = [&](int tk, int tv) __attribute__((always_inline)) {
-    int r = 0;
-    if (lane < 3) {
-      const int jk = (jt0 + tk) * KT, jv = (jt0 + tv) * KT;
-      r = page_of(lane < 2 ? k_key(jk, lane) : v_key(jv));
-    }
-    return r;
+    const int jk = (jt0 + tk) * KT, jv = (jt0 + tv) * KT;
+    return page_of(lane < 2 ? k_key(jk, lane) : v_key(jv));
   };
   auto settled = [](int v) {
     int r;
@@ -241,6 +237,9 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
       for (int e = 0; e < 8; ++e) v[e] = (jc + e >= kvl) ? (__bf16)0.0f : v[e];
       *cp = v;
     }
+    // the step's last LDS operations before its barrier: the lgkmcnt(3) wait
+    // there leaves the last three in flight, which would be these writes
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   };
 
   // ---- LDS operand addresses ----
@@ -348,33 +347,39 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
     f32x16& sc = sbuf[PAR];                // S(t)
     f32x16& sn = sbuf[SAME ? PAR : PAR ^ 1];  // S(t+1)
     const int j0 = (jt0 + t) * KT;  // first key of tile t
-    // page ids of the next step's loads: K(t+3) (lanes 0-1), V(t+2) (lane 2)
+    // The step's set-up runs after its first MFMA is issued, in that MFMA's
+    // shadow (before, ~40 instructions of it stood between the barrier and
+    // the first MFMA): the page ids of the next step's loads (K(t+3) in
+    // lanes 0-1, V(t+2) in lane 2) are fetched at the first QK op, the load
+    // offsets of this step and the tile mask after op 0.
     int pid_next = 0;
-    if (LK || LV) pid_next = fetch_pids(t + 3, t + 2);
     uint64_t kp[2] = {0, 0}, vp = 0;
-    if (LK) {
-      kp[0] = k_off(__builtin_amdgcn_readlane(pid, 0), j0 + 2 * KT, 0);
-      kp[1] = k_off(__builtin_amdgcn_readlane(pid, 1), j0 + 2 * KT, 1);
-    }
-    if (LV) vp = v_off(__builtin_amdgcn_readlane(pid, 2), j0 + KT);
-    // masked tiles (and a negative scale) scale and mask the scores up
-    // front; the exponentials below then use them as they are
     bool plain = true;
-    if (SM) {
-      plain = j0 >= full_lo && j0 <= full_hi && c2 >= 0.0f;
-      if (!plain) {
-        rare_path();
-        // register r holds key j0 + 16 (r / 8) + 8 h + r % 8
-        const int kb0_ = j0 + 8 * h - lo_n;
-        const unsigned span = (unsigned)(hi_n - lo_n);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const unsigned rel = (unsigned)(kb0_ + 16 * (r >> 3) + (r & 7));
-          sc[r] = rel <= span ? sc[r] * c2 : -__builtin_inff();
-        }
+    float cmul = c2;
+    auto setup = [&]() __attribute__((always_inline)) {
+      if (LK) {
+        kp[0] = k_off(__builtin_amdgcn_readlane(pid, 0), j0 + 2 * KT, 0);
+        kp[1] = k_off(__builtin_amdgcn_readlane(pid, 1), j0 + 2 * KT, 1);
       }
-    }
-    const float cmul = plain ? c2 : 1.0f;
+      if (LV) vp = v_off(__builtin_amdgcn_readlane(pid, 2), j0 + KT);
+      // masked tiles (and a negative scale) scale and mask the scores up
+      // front; the exponentials below then use them as they are
+      if (SM) {
+        plain = j0 >= full_lo && j0 <= full_hi && c2 >= 0.0f;
+        if (!plain) {
+          rare_path();
+          // register r holds key j0 + 16 (r / 8) + 8 h + r % 8
+          const int kb0_ = j0 + 8 * h - lo_n;
+          const unsigned span = (unsigned)(hi_n - lo_n);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const unsigned rel = (unsigned)(kb0_ + 16 * (r >> 3) + (r & 7));
+            sc[r] = rel <= span ? sc[r] * c2 : -__builtin_inff();
+          }
+        }
+        cmul = plain ? c2 : 1.0f;
+      }
+    };
     float mx = -__builtin_inff(), m_use = m_run, m_new = m_run;
     bool need = false;
     float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -416,9 +421,13 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
         }
       }
     };
-#pragma unroll
-    for (int i = 0; i < NOP; ++i) {
+    constexpr int FOP = (PV && QK) ? NV : 8;  // op that fetches the next step's page ids
+    static_assert(!(LK || LV) || NOP > FOP, "a step with loads has an op to fetch page ids at");
+    auto op = [&](int i) __attribute__((always_inline)) {
       if (i + AH < NOP) load_op(i + AH, pv_c, Vp, Kr, ka, va);
+      // the next step's first PV operands (V(t), published a step ago) in
+      // the last ops: their ring slots continue this step's
+      else if (SM) load_op(i + AH - NOP, std::true_type{}, Vc, Kw, 0, va);
       if (PV && i < NV) {
         oacc[i / NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[i % (AH + 1)], pb[i % NT],
                                                                 oacc[i / NT], 0, 0, 0);
@@ -428,22 +437,31 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
         else if (ks < KS - 1) mfma_qk(sn, ra[i % (AH + 1)], qf[ks]);
         else mfma_qk_last(sn, ra[i % (AH + 1)], qf[ks]);
       }
-      // loads: K(t+2) at ops 0 and 2 of the PV half, V(t+1) at the first
-      // even ops of the QK half (of the PV half in a step without one), so
-      // that the tile writes into LDS split between the halves
-      constexpr int LB = (PV && QK) ? NV : 4;
-      if (LK && (i == 0 || i == 2)) k_load_half(Kw, kp[i == 2], i == 2);
+      if ((LK || LV) && i == FOP) pid_next = fetch_pids(t + 3, t + 2);
+      // loads: K(t+2) at ops 2 and 4 of the PV half, V(t+1) at the first
+      // even ops of the QK half (ops 6.. in a step without one), so that the
+      // tile writes into LDS split between the halves
+      constexpr int LB = (PV && QK) ? NV : 6;
+      if (LK && (i == 2 || i == 4)) k_load_half(Kw, kp[i == 4], i == 4);
       if (LV && i >= LB && i <= LB + 14 && i % 2 == 0) v_load(Vn, vp, (i - LB) / 2);
       if (SM) sm_at(i);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    // op 0, the set-up in its MFMA's shadow, then the other ops (a step of
+    // one tile's softmax alone has none)
+    if constexpr (NOP > 0) op(0);
+    setup();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 1; i < NOP; ++i) op(i);
     if (SM) {
 #pragma unroll
       for (int i = NOP; i < SM_END; ++i) sm_at(i);
     }
     static_assert(!(LV || LK) || NOP >= 32, "a step with loads has at least 32 ops");
-    // the loads of this step landed: publish V(t+1) (zeroed past kv_len) and K(t+2)
-    __builtin_amdgcn_s_waitcnt(0);
+    // the loads of this step landed: publish V(t+1) (zeroed past kv_len) and
+    // K(t+2).  vmcnt(0) only: the next step's first operand reads stay in flight.
+    __builtin_amdgcn_s_waitcnt(0x0f70);
     if (LV) v_sanitize(Vn, j0 + KT);
     if (SM) {
       if (need) {
@@ -483,11 +501,12 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
         pb[q] = __builtin_bit_cast(bf16x8, v);
       }
     }
-    // first operands of the next step's PV: V(t), published a step ago
-    if (SM) {
-      const int va2 = opaque(vaddr0);
+    if constexpr (NOP == 0) {
+      // no ops to issue them in: the next step's first operands here
+      if (SM) {
 #pragma unroll
-      for (int i = 0; i < AH; ++i) load_op(i, std::true_type{}, Vc, Kw, 0, va2);
+        for (int i = 0; i < AH; ++i) load_op(i, std::true_type{}, Vc, Kw, 0, va);
+      }
     }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0xc37f);  // lgkmcnt(3): all but the three operand reads
