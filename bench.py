@@ -521,10 +521,12 @@ def main():
     wall = time.perf_counter() - t0
 
     # per-row figures: each row launched `steps` times in a block of its own,
-    # every launch between HIP events.  Interleaved with the HBM-bound rows
-    # and their cache-flush reads, the hd512 prefill measured up to 18% slower
-    # (1.29-1.31 ms against 1.09-1.11 ms on its own, on the same inputs), so a
-    # row's own figure is taken where only that row runs.
+    # every launch between HIP events.  The MFMA-bound prefills take a fixed
+    # number of shader cycles per launch, so their times follow the shader
+    # clock, which the part sets between about 1.6 and 2.1 GHz under load
+    # (hardware counters: the hd512 prefill at 1.08-1.26 ms for 2.02-2.03 M
+    # cycles); runs that include the HBM-bound rows and their flush reads
+    # tend to the lower clocks.
     evs = {r.name: [] for r in rows}
     for r in rows:
         r.run()
