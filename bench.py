@@ -17,9 +17,11 @@ workload (inputs resident in HBM before timing starts), all on one stream:
 
 `ms_per_step` is the wall time of one such step (K steps after W warmup
 steps).  The per-row figures come from each row launched K more times in a
-block of its own, every launch bracketed by HIP events on that stream; a 1 GiB
-buffer is read before every launch of an HBM-bound row (outside its events) so
-its bytes come from HBM, not from the 256 MB last-level cache.
+block of its own, timed with HIP events on that stream: the K launches of a
+compute-bound row back to back between one pair of events (their mean), each
+launch of an HBM-bound row between its own pair (their median), after a read
+of a 1 GiB buffer (outside the events) so that its bytes come from HBM, not
+from the 256 MB last-level cache.
 
 The JSON line's `value` is the windowed paged prefill's algorithmic TFLOP/s on
 the batch-8 workload (only (query, key) pairs inside the window count).  Per-row
@@ -520,23 +522,35 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # per-row figures: each row launched `steps` times in a block of its own,
-    # every launch between HIP events.  The MFMA-bound prefills take a fixed
-    # number of shader cycles per launch, so their times follow the shader
-    # clock, which the part sets between about 1.6 and 2.1 GHz under load
-    # (hardware counters: the hd512 prefill at 1.08-1.26 ms for 2.02-2.03 M
-    # cycles); runs that include the HBM-bound rows and their flush reads
-    # tend to the lower clocks.
+    # per-row figures: each row launched `steps` times in a block of its own.
+    # A row that is not HBM-bound runs its launches back to back between one
+    # pair of HIP events: the mean launch duration (an event pair around each
+    # launch adds ~5 us of dispatch and event overhead to every launch).  An
+    # HBM-bound row reads the flush buffer before every launch, so each launch
+    # has its own events and the row reports their median.  The MFMA-bound
+    # prefills take a fixed number of shader cycles per launch, so their
+    # times follow the shader clock, which the part sets between about 1.6
+    # and 2.1 GHz under load (hardware counters: the hd512 prefill at
+    # 1.08-1.26 ms for 2.02-2.03 M cycles); runs that include the HBM-bound
+    # rows and their flush reads tend to the lower clocks.
     evs = {r.name: [] for r in rows}
     for r in rows:
         r.run()
-        for _ in range(args.steps):
-            if r.hbm:
+        if r.hbm:
+            for _ in range(args.steps):
                 flush.sum()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                r.run()
+                e1.record()
+                evs[r.name].append((e0, e1))
+        else:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
-            r.run()
+            for _ in range(args.steps):
+                r.run()
             e1.record()
             evs[r.name].append((e0, e1))
     torch.cuda.synchronize()
@@ -544,15 +558,20 @@ def main():
     out_rows = {}
     for r in rows:
         ms = np.array([a.elapsed_time(b) for a, b in evs[r.name]])
-        med = float(np.median(ms))
-        rate = r.work / (med * 1e-3) / (1e12 if r.unit == "TFLOP/s" else 1e9)
+        if r.hbm:
+            t_ms, timing = float(np.median(ms)), "median of per-launch HIP events"
+        else:
+            t_ms, timing = float(ms[0]) / args.steps, "mean over back-to-back launches"
+        rate = r.work / (t_ms * 1e-3) / (1e12 if r.unit == "TFLOP/s" else 1e9)
         peak = PEAK_BF16_TFLOPS if r.unit == "TFLOP/s" else PEAK_HBM_GBS
         out_rows[r.name] = {"achieved": round(rate, 3), "unit": r.unit, "peak": peak,
                             "frac": round(rate / peak, 4), "bound": r.bound,
-                            "ms_median": round(med, 4), "ms_p10": round(float(np.percentile(ms, 10)), 4),
-                            "ms_p90": round(float(np.percentile(ms, 90)), 4),
+                            "ms": round(t_ms, 4), "timing": timing,
                             "work": r.work, "workload": r.desc}
-        log(f"{r.name:24s} {med * 1e3:9.1f} us  {rate:9.2f} {r.unit:8s} "
+        if r.hbm:
+            out_rows[r.name]["ms_p10"] = round(float(np.percentile(ms, 10)), 4)
+            out_rows[r.name]["ms_p90"] = round(float(np.percentile(ms, 90)), 4)
+        log(f"{r.name:24s} {t_ms * 1e3:9.1f} us  {rate:9.2f} {r.unit:8s} "
             f"({100 * rate / peak:5.1f}% of peak)")
 
     head = "prefill_window_hd256"
