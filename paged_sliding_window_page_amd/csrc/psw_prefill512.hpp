@@ -145,17 +145,9 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
   const PageRing ring = page_ring(last_page + 1, kvl, pshift);
 
   // ---- Q of this lane's row, B operands of the QK MFMAs ----
-  // lane (n, h), k-step ks: dims 16 ks + 8 h .. + 7 of row n
+  // lane (n, h), k-step ks: dims 16 ks + 8 h .. + 7 of row n; loaded in the
+  // prologue through LDS
   bf16x8 qf[KS];
-  {
-    const __bf16* qrow = P.q + ((int64_t)(q_beg + (row_valid ? tok : 0)) * P.num_qo_heads + head) * D +
-                         8 * h;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
-      qf[ks] = row_valid ? v : bf16x8{};
-    }
-  }
 
   // ---- tile loads (16 instructions of 1 KiB per K or V^T tile) ----
   // K: wave w loads keys 4 w .. 4 w + 3 of each of the tile's two 16-key
@@ -291,8 +283,30 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
   char* Vn = vb1;
   int pid = 0;        // page ids of this step's loads (lanes 0-2)
 
-  // ---- prologue: K(0), K(1), V(0) resident, S(0) = K(0) Q^T ----
+  // ---- prologue: Q, then K(0), K(1), V(0) resident, S(0) = K(0) Q^T ----
   {
+    // Q through LDS: wave w's 32 rows into a 32 KiB buffer of its own, one
+    // 1 KiB row per load instruction (lane l brings chunk l ^ (r % 16) of
+    // row r, so that the operand reads below, 32 rows at one chunk, hit
+    // distinct banks), then read back in the operand layout.  Loaded straight
+    // into registers, each load instruction touched 32 rows at 32 bytes and
+    // the loads took ~12 k cycles to issue.  A row past qo_len takes the
+    // request's first query (its output is never written).
+    char* const qst = w == 0 ? kb0 : w == 1 ? kb1 : w == 2 ? vb0 : vb1;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      const int tk = t0 + w * tok_w + (r >> gs);
+      const int hd = (kvh << gs) + (r & ((1 << gs) - 1));
+      const __bf16* row = P.q + ((int64_t)(q_beg + (tk < qo_len ? tk : 0)) * P.num_qo_heads + hd) * D;
+      lds_dma16_s(row, (uint32_t)((lane ^ (r & 15)) << 4), qst + r * 1024);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's rows landed
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qst + n * 1024 + (((2 * ks + h) ^ (n & 15)) << 4));
+    // every wave has its Q before the tiles overwrite the buffers
+    lds_barrier();
     const int j0 = jt0 * KT;
     const int pk0 = ldu(pages + ring(k_key(j0, 0) >> pshift));
     const int pk1 = ldu(pages + ring(k_key(j0, 1) >> pshift));
