@@ -531,7 +531,7 @@ def main():
     # prefills take a fixed number of shader cycles per launch, so their
     # times follow the shader clock, which the part sets between about 1.6
     # and 2.1 GHz under load (hardware counters: the hd512 prefill at
-    # 1.08-1.26 ms for 2.02-2.03 M cycles); runs that include the HBM-bound
+    # 1.08-1.26 ms for 2.00-2.03 M cycles); runs that include the HBM-bound
     # rows and their flush reads tend to the lower clocks.
     evs = {r.name: [] for r in rows}
     for r in rows:
