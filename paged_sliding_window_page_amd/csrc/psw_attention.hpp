@@ -1,19 +1,17 @@
-// Paged prefill attention for gfx950: bf16 MFMA, online softmax, K/V gathered
-// through a page table.  One kernel template serves
-//   * windowed paged prefill at head_dim 256 (PR "feat(kernels): Rust wrapper
-//     for the hd256 windowed paged prefill", Description: the caller passes
-//     sm_scale, the window bound is inclusive, and key addresses follow from
-//     the page table and the length of each request's final page),
-//   * full paged prefill at head_dim 512 (PR "feat(gemma4): paged KV serving
-//     across both attention families", Description: the global family has a
-//     single KV head of 512 dims and no window),
-//   * the split-KV form used when every request of a call has one query
-//     token (same PR, Description: serving decodes through the prefill entry),
-//     whose partial results are combined by merge_kernel.
+// Paged attention for gfx950: bf16 MFMA, online softmax, K/V gathered through
+// a page table.  This kernel template serves the split-KV form of one-token
+// decode when a GQA group is wider than the decode kernel's 16 query heads per
+// KV head (PR "feat(gemma4): paged KV serving across both attention
+// families", Description: serving decodes through the prefill entry), at head
+// dim 256 and 512; the pieces write partial results that merge_kernel
+// combines.  (The prefills have kernels of their own: psw_prefill_pp.hpp at
+// head_dim 256, psw_prefill512.hpp at head_dim 512; the template's non-split
+// form is not instantiated.)
 //
-// Work-group: 4 waves, 128 query rows = (128 / group) tokens x group heads of
-// one KV head, so the group's heads share every K/V tile.  Each wave owns 32
-// rows.  Per KV tile (64 keys at D=256, 32 at D=512):
+// Work-group: 4 waves of 32 query rows (at head_dim 512 two waves share a row
+// group, each with half the dims: 64 rows), rows = tokens x the group's heads
+// of one KV head, so the group's heads share every K/V tile.  Per KV tile (64
+// keys at D=256, 32 at D=512):
 //   S^T[key][row] = K Q^T     v_mfma_f32_32x32x16_bf16, K from LDS (A), Q in
 //                             registers (B)
 //   P = exp2(S*scale*log2e - m) with a lazily raised running max m
