@@ -197,19 +197,31 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
   auto v_off = [&](int page, int j0) __attribute__((always_inline)) {
     return page_off(page) + (uint32_t)((v_key(j0) & (psize - 1)) * 2);
   };
-  auto k_load_half = [&](char* kl, uint64_t koff, int half) __attribute__((always_inline)) {
+  // rows 2 p and 2 p + 1 (p = 0, 1) of the wave's four rows of one K half
+  auto k_load_pair = [&](char* kl, uint64_t koff, int half, int p) __attribute__((always_inline)) {
     const char* base = kbase_g + koff;
     const uint32_t m0 =
         (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(kl + (16 * half + 4 * w) * 1024);
-    asm volatile(
-        "s_mov_b32 m0, %4\n\t"
-        "global_load_lds_dwordx4 %0, %5\n\t"
-        "global_load_lds_dwordx4 %1, %5 offset:1024\n\t"
-        "global_load_lds_dwordx4 %2, %5 offset:2048\n\t"
-        "global_load_lds_dwordx4 %3, %5 offset:3072"
-        :
-        : "v"(kvo[0]), "v"(kvo[1]), "v"(kvo[2]), "v"(kvo[3]), "s"(m0), "s"(base)
-        : "memory", "m0");
+    if (p == 0)
+      asm volatile(
+          "s_mov_b32 m0, %2\n\t"
+          "global_load_lds_dwordx4 %0, %3\n\t"
+          "global_load_lds_dwordx4 %1, %3 offset:1024"
+          :
+          : "v"(kvo[0]), "v"(kvo[1]), "s"(m0), "s"(base)
+          : "memory", "m0");
+    else
+      asm volatile(
+          "s_mov_b32 m0, %2\n\t"
+          "global_load_lds_dwordx4 %0, %3 offset:2048\n\t"
+          "global_load_lds_dwordx4 %1, %3 offset:3072"
+          :
+          : "v"(kvo[2]), "v"(kvo[3]), "s"(m0), "s"(base)
+          : "memory", "m0");
+  };
+  auto k_load_half = [&](char* kl, uint64_t koff, int half) __attribute__((always_inline)) {
+    k_load_pair(kl, koff, half, 0);
+    k_load_pair(kl, koff, half, 1);
   };
   auto v_load = [&](char* vl, uint64_t voff, int j) __attribute__((always_inline)) {
     lds_dma16_s(vbase_g + voff, vvo[j], vl + (8 * w + j) * 1024);
@@ -452,11 +464,12 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
         else mfma_qk_last(sn, ra[i % (AH + 1)], qf[ks]);
       }
       if ((LK || LV) && i == FOP) pid_next = fetch_pids(t + 3, t + 2);
-      // loads: K(t+2) at ops 2 and 4 of the PV half, V(t+1) at the first
-      // even ops of the QK half (ops 6.. in a step without one), so that the
-      // tile writes into LDS split between the halves
+      // loads: K(t+2) two rows at a time at ops 2, 6, 10 and 14 of the PV
+      // half (four at ops 2 and 4: 1.2% slower), V(t+1) at the first even
+      // ops of the QK half (ops 6.. in a step without one), so that the tile
+      // writes into LDS split between the halves
       constexpr int LB = (PV && QK) ? NV : 6;
-      if (LK && (i == 2 || i == 4)) k_load_half(Kw, kp[i == 4], i == 4);
+      if (LK && i >= 2 && i <= 14 && i % 4 == 2) k_load_pair(Kw, kp[i >= 10], i >= 10, (i >> 2) & 1);
       if (LV && i >= LB && i <= LB + 14 && i % 2 == 0) v_load(Vn, vp, (i - LB) / 2);
       if (SM) sm_at(i);
       __builtin_amdgcn_sched_barrier(0);
