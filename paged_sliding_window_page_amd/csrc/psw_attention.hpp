@@ -661,20 +661,26 @@ __global__ __launch_bounds__(256, 1) void attention_kernel(AttnParams P) {
 //   O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,   M = max_s m_s.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(D / 4) void merge_kernel(MergeParams P) {
-  const int b = blockIdx.x / P.num_qo_heads;
-  const int head = blockIdx.x - b * P.num_qo_heads;
-  const int first = P.req_splits[2 * b];
-  const int ns = P.req_splits[2 * b + 1];
+  const int b = blockIdx.y;  // request of this launch
+  const int head = blockIdx.x;
+  const int first = P.req[3 * b];
+  const int ns = P.req[3 * b + 1];
+  const int qrow = P.req[3 * b + 2];
+  const int nh = P.num_qo_heads;
+  const float* const part_o = P.part_o;
+  const float* const part_ml = P.part_ml;
+  // every argument read in one round of loads, before the branch below
+  asm volatile("" ::"s"(first), "s"(ns), "s"(qrow), "s"(nh), "s"(part_o), "s"(part_ml));
   if (ns == 0) return;  // the decode kernel wrote this request's O itself
   // One pass with a running maximum: 16 splits at a time, all of their loads
   // issued first, so a request with up to 16 splits costs one memory round
-  // trip after its split list.
+  // trip after the launch arguments.
   constexpr int U = 16;
-  const float* ml = P.part_ml + ((int64_t)first * P.num_qo_heads + head) * 2;
-  const int64_t ml_stride = 2 * (int64_t)P.num_qo_heads;
+  const float* ml = part_ml + ((int64_t)first * nh + head) * 2;
+  const int64_t ml_stride = 2 * (int64_t)nh;
   const int d = 4 * threadIdx.x;
-  const float* po = P.part_o + ((int64_t)first * P.num_qo_heads + head) * D + d;
-  const int64_t po_stride = (int64_t)P.num_qo_heads * D;
+  const float* po = part_o + ((int64_t)first * nh + head) * D + d;
+  const int64_t po_stride = (int64_t)nh * D;
   float M = kNegBig, L = 0.0f;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int s0 = 0; s0 < ns; s0 += U) {
@@ -702,7 +708,7 @@ __global__ __launch_bounds__(D / 4) void merge_kernel(MergeParams P) {
     }
   }
   const float inv = 1.0f / L;
-  const int64_t orow = ((int64_t)P.qo_indptr[b] * P.num_qo_heads + head) * D + d;
+  const int64_t orow = ((int64_t)qrow * nh + head) * D + d;
   if constexpr (OUT_BF16) {
     bf16x4 v = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv), (__bf16)(acc[2] * inv),
                 (__bf16)(acc[3] * inv)};

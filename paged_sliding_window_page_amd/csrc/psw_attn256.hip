@@ -34,11 +34,25 @@ hipError_t launch_attention_d256(bool split, bool out_bf16, const AttnParams& p,
   return out_bf16 ? launch_one<false, true>(p, n_items, s) : launch_one<false, false>(p, n_items, s);
 }
 
-hipError_t launch_merge_d256(bool out_bf16, const MergeParams& p, int batch, hipStream_t s) {
-  const dim3 grid(batch * p.num_qo_heads);
-  if (out_bf16) hipLaunchKernelGGL((merge_kernel<256, true>), grid, dim3(256 / 4), 0, s, p);
-  else hipLaunchKernelGGL((merge_kernel<256, false>), grid, dim3(256 / 4), 0, s, p);
-  return hipGetLastError();
+hipError_t launch_merge_d256(bool out_bf16, MergeParams p, const int32_t* req_splits,
+                             const int32_t* qo_indptr, int batch, hipStream_t s) {
+  for (int b0 = 0; b0 < batch; b0 += kMergeReqsPerLaunch) {
+    const int n = batch - b0 < kMergeReqsPerLaunch ? batch - b0 : kMergeReqsPerLaunch;
+    bool any = false;
+    for (int i = 0; i < n; ++i) {
+      p.req[3 * i] = req_splits[2 * (b0 + i)];
+      p.req[3 * i + 1] = req_splits[2 * (b0 + i) + 1];
+      p.req[3 * i + 2] = qo_indptr[b0 + i];
+      any = any || p.req[3 * i + 1] > 0;
+    }
+    if (!any) continue;
+    const dim3 grid(p.num_qo_heads, n);
+    if (out_bf16) hipLaunchKernelGGL((merge_kernel<256, true>), grid, dim3(256 / 4), 0, s, p);
+    else hipLaunchKernelGGL((merge_kernel<256, false>), grid, dim3(256 / 4), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace psw_dev

@@ -72,13 +72,18 @@ __device__ __forceinline__ PageRing page_ring(int n_pages, int kv_len, int page_
   return r;
 }
 
+// Split-KV merge launch: up to kMergeReqsPerLaunch requests, whose split lists
+// travel in the launch's own arguments (a work-group reads them with its first
+// loads instead of a dependent load from memory).
+constexpr int kMergeReqsPerLaunch = 256;
 struct MergeParams {
   const float* part_o;
   const float* part_ml;
-  const int32_t* req_splits;  // pairs (first slot, count); count 0: O already written
-  const int32_t* qo_indptr;
   void* o;
   int32_t num_qo_heads;
+  // per request of the launch: first partial slot, number of pieces (0: the
+  // decode kernel wrote its O), output row
+  int32_t req[3 * kMergeReqsPerLaunch];
 };
 
 // Prep work item: (request, first global token, tokens (<= 16), page id,
@@ -120,8 +125,14 @@ hipError_t launch_prefill512(bool out_bf16, const AttnParams& p, int n_items, hi
 // as the split attention kernels).  Needs H_q / H_kv <= kDecodeMaxGroup.
 constexpr int kDecodeMaxGroup = 16;
 hipError_t launch_decode(int head_dim, const AttnParams& p, int n_wgs, hipStream_t s);
-hipError_t launch_merge_d256(bool out_bf16, const MergeParams& p, int batch, hipStream_t s);
-hipError_t launch_merge_d512(bool out_bf16, const MergeParams& p, int batch, hipStream_t s);
+// Merges the partials of every request of a batch that has pieces: p holds
+// the pointers and head count; req_splits (pairs: first slot, count) and
+// qo_indptr are the batch's host arrays, sent kMergeReqsPerLaunch requests per
+// launch (launches with no pieces to merge are skipped).
+hipError_t launch_merge_d256(bool out_bf16, MergeParams p, const int32_t* req_splits,
+                             const int32_t* qo_indptr, int batch, hipStream_t s);
+hipError_t launch_merge_d512(bool out_bf16, MergeParams p, const int32_t* req_splits,
+                             const int32_t* qo_indptr, int batch, hipStream_t s);
 hipError_t launch_prep_hd256(const PrepParams& p, int n_items, hipStream_t s);
 hipError_t launch_prep_hd512(const PrepParams& p, int n_items, hipStream_t s);
 hipError_t launch_prep_q_hd512(const PrepParams& p, int n_items, hipStream_t s);

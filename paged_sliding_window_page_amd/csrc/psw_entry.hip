@@ -39,8 +39,6 @@ struct psw_device_mirror {
   int64_t pf_wl = -3;
   int32_t* dc_items = nullptr;
   size_t dc_cap = 0;
-  int32_t* dc_req = nullptr;
-  size_t dc_req_cap = 0;
   uint64_t dc_gen = 0;
   int64_t dc_wl = -3;
   int32_t dc_mode = -1;
@@ -236,7 +234,6 @@ int run_attention(psw_plan* plan, const psw_pool* pool, int64_t layer, const voi
       std::vector<int32_t> table(plan->decode.items);
       table.insert(table.end(), plan->decode.wg_items.begin(), plan->decode.wg_items.end());
       rc = upload(m, &m->dc_items, &m->dc_cap, table, s);
-      if (!rc) rc = upload(m, &m->dc_req, &m->dc_req_cap, plan->decode.req_splits, s);
       if (rc) return rc;
       m->dc_gen = plan->generation;
       m->dc_wl = wle;
@@ -293,12 +290,12 @@ int run_attention(psw_plan* plan, const psw_pool* pool, int64_t layer, const voi
     psw_dev::MergeParams mp{};
     mp.part_o = p.part_o;
     mp.part_ml = p.part_ml;
-    mp.req_splits = m->dc_req;
-    mp.qo_indptr = p.qo_indptr;
     mp.o = o;
     mp.num_qo_heads = st.num_qo_heads;
-    e = head_dim == 256 ? psw_dev::launch_merge_d256(o_dtype == 1, mp, st.batch, s)
-                        : psw_dev::launch_merge_d512(o_dtype == 1, mp, st.batch, s);
+    const int32_t* rs = plan->decode.req_splits.data();
+    e = head_dim == 256
+            ? psw_dev::launch_merge_d256(o_dtype == 1, mp, rs, st.qo_indptr.data(), st.batch, s)
+            : psw_dev::launch_merge_d512(o_dtype == 1, mp, rs, st.qo_indptr.data(), st.batch, s);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
   return PSW_OK;
@@ -347,7 +344,7 @@ void psw_mirror_free(psw_device_mirror* m, psw_stream_t stream) {
   // or copy uses the buffers below
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipStreamSynchronize(s);
-  for (void* p : {(void*)m->meta, (void*)m->pf_items, (void*)m->dc_items, (void*)m->dc_req,
+  for (void* p : {(void*)m->meta, (void*)m->pf_items, (void*)m->dc_items,
                   (void*)m->prep, (void*)m->part, (void*)m->err})
     if (p) (void)hipFreeAsync(p, s);
   for (psw_stage_slot& sl : m->slots) {

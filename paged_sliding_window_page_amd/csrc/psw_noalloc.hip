@@ -86,7 +86,7 @@ extern "C" int paged_decode_hd512_noalloc(psw_plan* plan, const psw_pool* pool, 
   if (rc) return rc;
 
   // layout: qo_indptr | kv_page_indptr | kv_page_indices | kv_len | items |
-  // wg_items | req_splits | partial O | partial (max, sum), 256-byte aligned
+  // wg_items | partial O | partial (max, sum), 256-byte aligned
   const size_t B = size_t(st.batch);
   size_t off = 0;
   const size_t o_qo = off;
@@ -99,8 +99,6 @@ extern "C" int paged_decode_hd512_noalloc(psw_plan* plan, const psw_pool* pool, 
   off = align256(off + B * 4);
   const size_t o_items = off;
   off = align256(off + (ds.items.size() + ds.wg_items.size()) * 4);
-  const size_t o_req = off;
-  off = align256(off + ds.req_splits.size() * 4);
   const size_t o_part = off;
   const size_t n_part = size_t(ds.num_partials) * st.num_qo_heads;
   off = align256(off + n_part * D * 4);
@@ -135,8 +133,7 @@ extern "C" int paged_decode_hd512_noalloc(psw_plan* plan, const psw_pool* pool, 
       const Part parts[] = {{o_qo, &st.qo_indptr}, {o_kvp, &st.kv_page_indptr},
                             {o_idx, &st.kv_page_indices}, {o_len, &st.kv_len},
                             {o_items, &ds.items},
-                            {o_items + ds.items.size() * 4, &ds.wg_items},
-                            {o_req, &ds.req_splits}};
+                            {o_items + ds.items.size() * 4, &ds.wg_items}};
       for (const Part& pt : parts) {
         if (pt.v->empty()) continue;
         e = hipMemcpyAsync(base + pt.off, pt.v->data(), pt.v->size() * 4,
@@ -189,11 +186,10 @@ extern "C" int paged_decode_hd512_noalloc(psw_plan* plan, const psw_pool* pool, 
     psw_dev::MergeParams mp{};
     mp.part_o = p.part_o;
     mp.part_ml = p.part_ml;
-    mp.req_splits = reinterpret_cast<const int32_t*>(base + o_req);
-    mp.qo_indptr = p.qo_indptr;
     mp.o = o;
     mp.num_qo_heads = st.num_qo_heads;
-    e = psw_dev::launch_merge_d512(o_dtype == 1, mp, st.batch, s);
+    e = psw_dev::launch_merge_d512(o_dtype == 1, mp, ds.req_splits.data(), st.qo_indptr.data(),
+                                   st.batch, s);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
   return PSW_OK;
