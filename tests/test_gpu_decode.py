@@ -157,6 +157,19 @@ def test_decode_entries_each_form(hd, mode, out_dtype):
 
 
 @pytest.mark.parametrize("hd", [256, 512])
+def test_decode_merge_past_256_requests(hd):
+    """Split form on 300 requests: the merge runs in launches of 256 requests
+    (each request's split list travels in its launch's arguments), so the cut
+    requests past the first 256 go through a second launch."""
+    kv = [24 + (97 * i) % 200 for i in range(300)]
+    case = _case(hd, 81, kv)
+    wl = 100 if hd == 256 else -1
+    gpu = _run_decode_entry(case, 1, wl, torch.float32)
+    check_close(gpu, oracle_attention(case, window_left=wl, threads=8),
+                f"decode 300 requests hd{hd}")
+
+
+@pytest.mark.parametrize("hd", [256, 512])
 def test_decode_forms_agree_on_short_requests(hd):
     """Short requests (the automatic choice takes the direct form): direct and
     split give the same result within the gate, and both match the oracle."""
