@@ -64,7 +64,7 @@ def test_group_sizes(hq, hkv):
     check_close(gpu, oracle_attention(case, window_left=50), f"group {hq // hkv}")
 
 
-@pytest.mark.parametrize("page_size", [8, 32, 64, 256])
+@pytest.mark.parametrize("page_size", [8, 32, 64, 256, 1024])
 def test_page_sizes(page_size):
     case = _local(13, [90, 33], [150, 200], page_size=page_size)
     gpu = run_attention(case, window_left=70, label=f"P={page_size}")
@@ -195,7 +195,7 @@ def test_hd512_full_prefill(qo, kv):
     check_close(gpu, oracle_attention(case), f"hd512 {qo}")
 
 
-@pytest.mark.parametrize("page_size", [8, 32, 64])
+@pytest.mark.parametrize("page_size", [8, 32, 64, 1024])
 def test_hd512_page_sizes(page_size):
     """Page sizes other than 16 (per-round page lookup, a tile spanning part of
     a page or several pages)."""

@@ -37,7 +37,7 @@ KV_MIX = [1, 2, 15, 16, 17, 31, 32, 33, 64, 65, 300, 1500]
 
 
 @pytest.mark.parametrize("hd", [256, 512])
-@pytest.mark.parametrize("page_size", [8, 16, 32, 64])
+@pytest.mark.parametrize("page_size", [8, 16, 32, 64, 1024])
 def test_decode_page_sizes(hd, page_size):
     case = _case(hd, 61, KV_MIX, page_size=page_size)
     wl = 100 if hd == 256 else -1
