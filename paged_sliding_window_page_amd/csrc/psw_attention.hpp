@@ -52,6 +52,12 @@ __device__ __forceinline__ int kswz(int key) {
   return (key & 3) | ((key >> 1) & 4) | ((key << 1) & 8);
 }
 
+// The tile loads below write m0 and name it among their clobbers; clang
+// treats m0 as reserved and warns that it may not be preserved across the
+// statement, which is what the clobber says.  The warning is silenced here
+// only.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 // global_load_lds_dwordx4 issued as inline assembly: 16 bytes per lane from
 // gsrc into LDS at lds_base + 16 * lane.  The compiler does not track these
 // loads: a kernel that uses them orders them itself, with explicit vmcnt
@@ -75,6 +81,7 @@ __device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, co
                : "v"(voff), "s"(sbase), "s"(m0)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 __device__ __forceinline__ void lds_load16(const void* gsrc, void* ldst) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,

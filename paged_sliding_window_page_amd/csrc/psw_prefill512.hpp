@@ -85,7 +85,6 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
   constexpr int NV = NT * DB;       // PV MFMAs per tile (32)
   constexpr int TILE = KT * D * 2;  // 32 KiB
   constexpr int AH = 3;             // LDS operand reads in flight ahead of the MFMAs
-  constexpr int NWAVE = 4;
   // O and the row sums are rescaled only when a row's maximum rises by more
   // than kSlack (log2 units) over the one they are scaled to: P stays below
   // 2^16 and the rescale (256 accumulators) is rare.
@@ -198,6 +197,9 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
     return page_off(page) + (uint32_t)((v_key(j0) & (psize - 1)) * 2);
   };
   // rows 2 p and 2 p + 1 (p = 0, 1) of the wave's four rows of one K half
+  // (m0 clobbered: see the tile-load helpers in psw_attention.hpp)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
   auto k_load_pair = [&](char* kl, uint64_t koff, int half, int p) __attribute__((always_inline)) {
     const char* base = kbase_g + koff;
     const uint32_t m0 =
@@ -219,6 +221,7 @@ __global__ __launch_bounds__(256, 1) void prefill512_kernel(AttnParams P) {
           : "v"(kvo[2]), "v"(kvo[3]), "s"(m0), "s"(base)
           : "memory", "m0");
   };
+#pragma clang diagnostic pop
   auto k_load_half = [&](char* kl, uint64_t koff, int half) __attribute__((always_inline)) {
     k_load_pair(kl, koff, half, 0);
     k_load_pair(kl, koff, half, 1);
