@@ -140,6 +140,21 @@ def test_hd512_prep_placement_and_values(qo, start):
     _check_prep(case, 512, g, pool, None)
 
 
+@pytest.mark.parametrize("d", [256, 512])
+@pytest.mark.parametrize("page_size", [8, 32, 64])
+def test_prep_page_sizes(d, page_size):
+    """Pages other than 16 slots: items of up to 8 tokens filling whole pages
+    (8-slot pages), or several items per page starting mid-page (32 and 64),
+    so the dim-major V stores take both their 8-slot-run form and the
+    element-wise one."""
+    case = synth.prep_case(80 + page_size, [5, 33, 16, 1, 70], [11, 0, 48, 300, 3], head_dim=d,
+                           num_kv_heads=8 if d == 256 else 1, num_layers=2, layer=1,
+                           page_size=page_size, extra_pages=3, with_q_v=d == 256,
+                           rope_positions=512)
+    g, pool, q_out = _run_prep(case, d, f"P={page_size}")
+    _check_prep(case, d, g, pool, q_out)
+
+
 def test_hd512_unit_weight_position_zero_k_equals_v_bitwise():
     case = synth.prep_case(71, [3], [0], head_dim=512, num_kv_heads=1, num_layers=1, layer=0,
                            with_q_v=False, rope_positions=64)
