@@ -91,6 +91,9 @@ def test_plan_info_records_bounds():
     (dict(kv_page_indptr=[0, 2, 2]), "PSW_E_SHAPE"),              # request without pages
     (dict(qo_indptr=[0, 30, 31]), "PSW_E_SHAPE"),                 # kv_len < qo_len
     (dict(page_size=12), "PSW_E_SHAPE"),
+    (dict(page_size=2048), "PSW_E_SHAPE"),                        # past the largest page
+    (dict(qo_indptr=[0], kv_page_indptr=[0], kv_page_indices=[],  # empty batch
+          kv_last_page_len=[]), "PSW_E_SHAPE"),
     (dict(num_qo_heads=2 ** 31), "PSW_E_OVERFLOW"),
     (dict(tile_q_override=-1), "PSW_E_OVERFLOW"),
 ])
